@@ -1,0 +1,1 @@
+"""Oracle package (test infrastructure only; never imported by the product path)."""

@@ -1,0 +1,384 @@
+// Oracle for the fused Mixture-of-Experts layer forward -- TEST INFRASTRUCTURE ONLY.
+//
+// A plain, slow, obviously-correct CPU implementation of what the GPU path
+// computes.  Only the tests, the smoke check and the benchmark's CPU-baseline
+// leg may load it; the product path never does.  It shares no code, header or
+// table with the HIP kernels.
+//
+// Sources (web pages describing HPC-Ops and the Hy4-preview MoE block):
+//  * "HPC-Ops - Tencent Hunyuan open-source inference operator library"
+//    (bestaitool.cc), sections "Main functions" and "Technical principles":
+//    FusedMoE is the five-stage chain routing index -> Gate-Up GEMM ->
+//    activation quantisation -> Down GEMM -> top-k weighted combine; the
+//    router GEMM emulates FP32 with a high BF16 part plus a residual BF16 part
+//    scaled by 1/256, combined with one FMA.
+//  * "PR #54160 report: [Hy4] support Hy4-preview model" (prhub.com.cn),
+//    section "Features and motivation": 256 routed experts, top-8, plus one
+//    shared expert; section "Implementation" item 4: FP8 blockwise 128x128
+//    weight scales.
+// Fused and unfused MoE compute the same function; the fusion only removes
+// memory movement and launches.  So this file is the plain layer definition
+// in double precision, with the FP8 quantisation steps emulated exactly.
+//
+// Readings where the pages are silent (each one listed in the design notes):
+//  * gate: softmax over the k selected logits; ties broken by lower expert id;
+//    ids stored in rank order (value desc, id asc); no capacity limit.
+//  * shared expert: SwiGLU of the same size, added with weight 1.
+//  * SwiGLU: h = SiLU(x.w1^T) * (x.w3^T), SiLU(z) = z / (1 + e^-z); w1 = gate.
+//  * FP8 = OCP E4M3FN (max 448, no infinities), round to nearest even,
+//    saturating.  Scale of a group/block = amax / 448 in fp32 (1 if amax = 0);
+//    code = encode(fp32(v / scale)).
+//  * router split: hi = bf16_rne(w), lo = bf16_rne((w - hi) * 256),
+//    logits = acc_hi + acc_lo / 256.
+//
+// Parity pins for every function here live in tests/test_oracle_*.py.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+double bf16_value(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Nearest bfloat16 to a finite float, ties to the even pattern.  The two
+// candidates are the float with its low 16 bits cleared (same sign, smaller or
+// equal magnitude) and the next bfloat16 of larger magnitude.
+uint16_t bf16_nearest(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  uint16_t down = static_cast<uint16_t>(u >> 16);
+  uint16_t up = static_cast<uint16_t>(down + 1);
+  double dv = v;
+  double e_down = std::fabs(dv - bf16_value(down));
+  double e_up = std::fabs(bf16_value(up) - dv);
+  if (e_down < e_up) return down;
+  if (e_up < e_down) return up;
+  return (down & 1u) ? up : down;
+}
+
+// OCP 8-bit floating point, E4M3FN: bias 7, 3 mantissa bits, exponent field 0
+// is subnormal (m/8 * 2^-6), pattern S.1111.111 is NaN, no infinities.
+double e4m3_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = (e == 0) ? std::ldexp(m / 8.0, -6) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+// Round a finite value to E4M3FN: nearest representable magnitude, ties to
+// even mantissa, magnitudes at or above 448 saturate to 448 (0x7E).
+uint8_t e4m3_code(float v) {
+  double a = std::fabs(static_cast<double>(v));
+  uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  if (a >= 448.0) return sign | 0x7E;
+  double quantum;
+  if (a < std::ldexp(1.0, -6)) {
+    quantum = std::ldexp(1.0, -9);               // subnormal spacing
+  } else {
+    int ex;
+    std::frexp(a, &ex);                           // a = f * 2^ex, f in [0.5, 1)
+    quantum = std::ldexp(1.0, (ex - 1) - 3);      // 3 mantissa bits in binade 2^(ex-1)
+  }
+  double q = std::nearbyint(a / quantum) * quantum;  // default mode: ties to even
+  if (q == 0.0) return sign;
+  int ex;
+  std::frexp(q, &ex);
+  int eb = ex - 1;                                // q in [2^eb, 2^(eb+1))
+  if (eb < -6) {                                  // subnormal
+    int m = static_cast<int>(q / std::ldexp(1.0, -9));
+    return sign | static_cast<uint8_t>(m);
+  }
+  int m = static_cast<int>(q / std::ldexp(1.0, eb) * 8.0) - 8;
+  return sign | static_cast<uint8_t>(((eb + 7) << 3) | m);
+}
+
+double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+template <class F>
+void parallel_for(int64_t n, int nthreads, F f) {
+  if (nthreads <= 1 || n <= 1) {
+    for (int64_t i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::vector<std::thread> pool;
+  int64_t nt = std::min<int64_t>(nthreads, n);
+  for (int64_t w = 0; w < nt; ++w)
+    pool.emplace_back([=] {
+      for (int64_t i = w; i < n; i += nt) f(i);
+    });
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+// ---------------------------------------------------------------- codecs
+double orc_bf16_value(uint16_t b) { return bf16_value(b); }
+uint16_t orc_bf16_nearest(float v) { return bf16_nearest(v); }
+double orc_e4m3_value(uint8_t c) { return e4m3_value(c); }
+uint8_t orc_e4m3_code(float v) { return e4m3_code(v); }
+
+void orc_e4m3_code_array(const float* v, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_code(v[i]);
+}
+
+// ---------------------------------------------------------------- router
+// HPC-Ops page, "Router GEMM" (main functions, technical principles): split an
+// fp32 weight offline into a high bf16 part and a residual bf16 part scaled by
+// 256 so that w ~= hi + lo / 256.
+void orc_router_split(const float* w, int64_t n, uint16_t* hi, uint16_t* lo) {
+  for (int64_t i = 0; i < n; ++i) {
+    hi[i] = bf16_nearest(w[i]);
+    float resid = w[i] - static_cast<float>(bf16_value(hi[i]));  // exact in fp32
+    lo[i] = bf16_nearest(resid * 256.0f);                       // power of two: exact
+  }
+}
+
+// Exact router logits in double: logits[t,e] = sum_h x[t,h] * w[e,h], with x
+// bf16 and w fp32 taken at their exact values.
+void orc_router_logits(const uint16_t* x, const float* w, int64_t T, int H, int E,
+                       double* logits, int nthreads) {
+  parallel_for(T, nthreads, [&](int64_t t) {
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h) acc += bf16_value(x[t * H + h]) * static_cast<double>(w[(int64_t)e * H + h]);
+      logits[t * E + e] = acc;
+    }
+  });
+}
+
+// ---------------------------------------------------------------- route
+// Stage 1 of FusedMoE ("routing index").  Per token: optional per-expert bias
+// added in fp32 (only on rows whose bias_rows flag is set, or on every row if
+// bias_rows is NULL), then the k experts with the largest biased logits,
+// ordered by (value desc, id asc), and weights = softmax over those k values.
+void orc_route(const float* logits, const float* bias, const uint8_t* bias_rows,
+               int64_t T, int E, int k, int32_t* ids, double* weights) {
+  std::vector<std::pair<float, int>> row(E);
+  for (int64_t t = 0; t < T; ++t) {
+    bool biased = bias != nullptr && (bias_rows == nullptr || bias_rows[t] != 0);
+    for (int e = 0; e < E; ++e) {
+      float l = logits[t * E + e];
+      if (biased) l = l + bias[e];
+      row[e] = {l, e};
+    }
+    std::sort(row.begin(), row.end(), [](const std::pair<float, int>& a, const std::pair<float, int>& b) {
+      if (a.first != b.first) return a.first > b.first;
+      return a.second < b.second;
+    });
+    double top = row[0].first, denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += std::exp(static_cast<double>(row[j].first) - top);
+    for (int j = 0; j < k; ++j) {
+      ids[t * k + j] = row[j].second;
+      weights[t * k + j] = std::exp(static_cast<double>(row[j].first) - top) / denom;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- align
+// HPC-Ops page, "FusedMoE pipeline": per-expert counts and a contiguous output
+// interval per expert.  Counting sort of the P = T*k (token, rank) pairs by
+// expert, stable in pair order (hence ascending token inside each expert).
+// offsets[0..E] is the exclusive prefix sum of counts; offsets[E+1] adds the
+// shared expert's T rows (group E) when shared != 0.
+void orc_align(const int32_t* ids, int64_t T, int E, int k, int shared, int32_t* counts,
+               int32_t* offsets, int32_t* slot_pair, int32_t* pair_slot) {
+  int64_t P = T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[ids[p]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  offsets[E + 1] = offsets[E] + (shared ? static_cast<int32_t>(T) : 0);
+  std::vector<int32_t> next(offsets, offsets + E);
+  for (int64_t p = 0; p < P; ++p) {
+    int32_t s = next[ids[p]]++;
+    slot_pair[s] = static_cast<int32_t>(p);
+    pair_slot[p] = s;
+  }
+}
+
+// ---------------------------------------------------------------- fp8 quant
+// Activation quantisation: per row, per group of 128 columns,
+// scale = amax / 448 (fp32 division), code = e4m3(fp32(x / scale)).
+void orc_quant_rows_fp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s) {
+  int groups = cols / 128;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int g = 0; g < groups; ++g) {
+      float amax = 0.0f;
+      for (int i = 0; i < 128; ++i)
+        amax = std::max(amax, static_cast<float>(std::fabs(bf16_value(x[r * cols + g * 128 + i]))));
+      float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      s[r * groups + g] = sc;
+      for (int i = 0; i < 128; ++i) {
+        float v = static_cast<float>(bf16_value(x[r * cols + g * 128 + i])) / sc;
+        q[r * cols + g * 128 + i] = e4m3_code(v);
+      }
+    }
+}
+
+// Weight quantisation with 128x128 block scales (PR #54160 report,
+// implementation item 4): for each matrix [rows, cols] and each 128x128 block,
+// scale = amax / 448 (fp32), code = e4m3(fp32(w / scale)).  s has shape
+// [mats, rows/128, cols/128].
+void orc_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s) {
+  int rb = rows / 128, cb = cols / 128;
+  for (int64_t m = 0; m < mats; ++m)
+    for (int bi = 0; bi < rb; ++bi)
+      for (int bj = 0; bj < cb; ++bj) {
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i)
+          for (int j = 0; j < 128; ++j) {
+            int64_t idx = (m * rows + bi * 128 + i) * (int64_t)cols + bj * 128 + j;
+            amax = std::max(amax, static_cast<float>(std::fabs(bf16_value(w[idx]))));
+          }
+        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        s[(m * rb + bi) * cb + bj] = sc;
+        for (int i = 0; i < 128; ++i)
+          for (int j = 0; j < 128; ++j) {
+            int64_t idx = (m * rows + bi * 128 + i) * (int64_t)cols + bj * 128 + j;
+            q[idx] = e4m3_code(static_cast<float>(bf16_value(w[idx])) / sc);
+          }
+      }
+}
+
+// ---------------------------------------------------------------- expert FFN
+// One SwiGLU expert on one token, bf16 operands, everything else in double:
+// g = x.w1^T, u = x.w3^T, h = SiLU(g) * u, y = h.w2^T.
+// w1, w3: [I, H]; w2: [H, I].  h_out (may be NULL): [I]; y: [H].
+void orc_expert_bf16(const uint16_t* x, const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                     int H, int I, double* h_out, double* y) {
+  std::vector<double> xv(H), h(I);
+  for (int i = 0; i < H; ++i) xv[i] = bf16_value(x[i]);
+  for (int n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int i = 0; i < H; ++i) {
+      g += xv[i] * bf16_value(w1[(int64_t)n * H + i]);
+      u += xv[i] * bf16_value(w3[(int64_t)n * H + i]);
+    }
+    h[n] = silu(g) * u;
+    if (h_out) h_out[n] = h[n];
+  }
+  for (int m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int n = 0; n < I; ++n) acc += h[n] * bf16_value(w2[(int64_t)m * I + n]);
+    y[m] = acc;
+  }
+}
+
+// Blockwise-scaled fp8 dot product of one activation row with one weight row:
+// sum over 128-wide K blocks of (xs[kb] * ws[kb]) * sum_k dec(xq[k]) * dec(wq[k]).
+static double fp8_dot(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int K) {
+  double acc = 0.0;
+  for (int kb = 0; kb < K / 128; ++kb) {
+    double part = 0.0;
+    for (int i = 0; i < 128; ++i) part += e4m3_value(xq[kb * 128 + i]) * e4m3_value(wq[kb * 128 + i]);
+    acc += static_cast<double>(xs[kb]) * static_cast<double>(ws[kb]) * part;
+  }
+  return acc;
+}
+
+// One SwiGLU expert on one token with FP8 operands (the "activation
+// quantisation" stage of FusedMoE between Gate-Up and Down):
+//  xq [H] e4m3 + xs [H/128]; w1q, w3q [I, H] e4m3 + s1, s3 [I/128, H/128];
+//  w2q [H, I] e4m3 + s2 [H/128, I/128].
+// g, u are blockwise-scaled sums in double; h = SiLU(g) * u is rounded to
+// fp32 and requantised per 128 columns (scale amax/448); y uses those codes.
+// h_out (may be NULL) receives the fp32-rounded h; y: [H].
+void orc_expert_fp8(const uint8_t* xq, const float* xs, const uint8_t* w1q, const float* s1,
+                    const uint8_t* w3q, const float* s3, const uint8_t* w2q, const float* s2,
+                    int H, int I, double* h_out, double* y) {
+  int hb = H / 128, ib = I / 128;
+  std::vector<float> h(I);
+  std::vector<float> ws(hb);
+  for (int n = 0; n < I; ++n) {
+    for (int kb = 0; kb < hb; ++kb) ws[kb] = s1[(n / 128) * hb + kb];
+    double g = fp8_dot(xq, xs, w1q + (int64_t)n * H, ws.data(), H);
+    for (int kb = 0; kb < hb; ++kb) ws[kb] = s3[(n / 128) * hb + kb];
+    double u = fp8_dot(xq, xs, w3q + (int64_t)n * H, ws.data(), H);
+    h[n] = static_cast<float>(silu(g) * u);
+    if (h_out) h_out[n] = h[n];
+  }
+  std::vector<uint8_t> hq(I);
+  std::vector<float> hs(ib);
+  for (int g = 0; g < ib; ++g) {
+    float amax = 0.0f;
+    for (int i = 0; i < 128; ++i) amax = std::max(amax, std::fabs(h[g * 128 + i]));
+    float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    hs[g] = sc;
+    for (int i = 0; i < 128; ++i) hq[g * 128 + i] = e4m3_code(h[g * 128 + i] / sc);
+  }
+  std::vector<float> w2s(ib);
+  for (int m = 0; m < H; ++m) {
+    for (int kb = 0; kb < ib; ++kb) w2s[kb] = s2[(m / 128) * ib + kb];
+    y[m] = fp8_dot(hq.data(), hs.data(), w2q + (int64_t)m * I, w2s.data(), I);
+  }
+}
+
+// ---------------------------------------------------------------- layer
+// Expert weights for the layer.  bf16 weights (wtype 0) or e4m3 codes with
+// 128x128 fp32 block scales (wtype 1).  Routed experts are [E, ...]; the
+// shared expert (has_shared) is a single expert of the same shape.
+struct orc_layer {
+  int wtype, E, H, I, has_shared;
+  const void *w1, *w3, *w2;
+  const float *s1, *s3, *s2;
+  const void *sw1, *sw3, *sw2;
+  const float *ss1, *ss3, *ss2;
+};
+
+// The whole layer on a list of tokens ("top-k weighted combine", stage 5):
+//   out[r] = sum_j w[t,j] * FFN_{ids[t,j]}(x_t) + FFN_shared(x_t),  t = rows[r].
+// bf16 path: x is bf16 [T,H] and xs is NULL.  fp8 path: x is the e4m3 code
+// array [T,H] and xs [T,H/128] its scales (from orc_quant_rows_fp8).
+// ids / weights are the route output [T,k].  out: [nrows, H] double.
+void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const int32_t* ids,
+                    const double* weights, int k, const int64_t* rows, int64_t nrows, double* out,
+                    int nthreads) {
+  const int H = L->H, I = L->I;
+  const int64_t mat = (int64_t)I * H;
+  const int64_t blk = (int64_t)(I / 128) * (H / 128);
+  parallel_for(nrows, nthreads, [&](int64_t r) {
+    int64_t t = rows[r];
+    std::vector<double> y(H);
+    double* o = out + r * H;
+    for (int m = 0; m < H; ++m) o[m] = 0.0;
+    int nexp = k + (L->has_shared ? 1 : 0);
+    for (int j = 0; j < nexp; ++j) {
+      bool shared = j == k;
+      int e = shared ? 0 : ids[t * k + j];
+      double wt = shared ? 1.0 : weights[t * k + j];
+      if (L->wtype == 0) {
+        const uint16_t* xr = static_cast<const uint16_t*>(x) + t * H;
+        const uint16_t* w1 = shared ? static_cast<const uint16_t*>(L->sw1) : static_cast<const uint16_t*>(L->w1) + e * mat;
+        const uint16_t* w3 = shared ? static_cast<const uint16_t*>(L->sw3) : static_cast<const uint16_t*>(L->w3) + e * mat;
+        const uint16_t* w2 = shared ? static_cast<const uint16_t*>(L->sw2) : static_cast<const uint16_t*>(L->w2) + e * mat;
+        orc_expert_bf16(xr, w1, w3, w2, H, I, nullptr, y.data());
+      } else {
+        const uint8_t* xr = static_cast<const uint8_t*>(x) + t * H;
+        const float* xsr = xs + t * (H / 128);
+        const uint8_t* w1 = shared ? static_cast<const uint8_t*>(L->sw1) : static_cast<const uint8_t*>(L->w1) + e * mat;
+        const uint8_t* w3 = shared ? static_cast<const uint8_t*>(L->sw3) : static_cast<const uint8_t*>(L->w3) + e * mat;
+        const uint8_t* w2 = shared ? static_cast<const uint8_t*>(L->sw2) : static_cast<const uint8_t*>(L->w2) + e * mat;
+        const float* s1 = shared ? L->ss1 : L->s1 + e * blk;
+        const float* s3 = shared ? L->ss3 : L->s3 + e * blk;
+        const float* s2 = shared ? L->ss2 : L->s2 + e * blk;
+        orc_expert_fp8(xr, xsr, w1, s1, w3, s3, w2, s2, H, I, nullptr, y.data());
+      }
+      for (int m = 0; m < H; ++m) o[m] += wt * y[m];
+    }
+  });
+}
+
+int orc_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+"""Oracle for the fused MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Python (ctypes + numpy) front end of ``moe_oracle.cpp``, a plain double
+precision CPU implementation of the layer that shares no code with the HIP
+path.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module; the product package never does.
+
+Every function takes and returns host numpy arrays.  bf16 data is carried as
+``uint16`` bit patterns and e4m3 data as ``uint8`` codes.  See the C++ file for
+the passages of the pages each function follows and for the readings taken
+where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+
+
+def build() -> str:
+    """Compile the oracle with the host C++ compiler (plain -O2, no fast-math)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+                           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("wtype", _I32), ("E", _I32), ("H", _I32), ("I", _I32), ("has_shared", _I32),
+                ("w1", _P), ("w3", _P), ("w2", _P), ("s1", _P), ("s3", _P), ("s2", _P),
+                ("sw1", _P), ("sw3", _P), ("sw2", _P), ("ss1", _P), ("ss3", _P), ("ss2", _P)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.orc_bf16_value.restype = ctypes.c_double
+        L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_nearest.restype = ctypes.c_uint16
+        L.orc_bf16_nearest.argtypes = [ctypes.c_float]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_code.restype = ctypes.c_uint8
+        L.orc_e4m3_code.argtypes = [ctypes.c_float]
+        L.orc_e4m3_code_array.argtypes = [_P, _I64, _P]
+        L.orc_router_split.argtypes = [_P, _I64, _P, _P]
+        L.orc_router_logits.argtypes = [_P, _P, _I64, _I32, _I32, _P, _I32]
+        L.orc_route.argtypes = [_P, _P, _P, _I64, _I32, _I32, _P, _P]
+        L.orc_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
+        L.orc_quant_rows_fp8.argtypes = [_P, _I64, _I32, _P, _P]
+        L.orc_quant_blocks_fp8.argtypes = [_P, _I64, _I32, _I32, _P, _P]
+        L.orc_expert_bf16.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _P]
+        L.orc_expert_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P]
+        L.orc_layer_rows.argtypes = [ctypes.POINTER(_Layer), _P, _P, _P, _P, _I32, _P, _I64, _P, _I32]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_P)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# ------------------------------------------------------------------ codecs
+def bf16_value(bits):
+    bits = _c(bits, np.uint16)
+    return np.array([lib().orc_bf16_value(int(b)) for b in bits.ravel()]).reshape(bits.shape)
+
+
+def e4m3_value(codes):
+    codes = _c(codes, np.uint8)
+    return np.array([lib().orc_e4m3_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e4m3_code(values):
+    v = _c(values, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3_code_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------------ router
+def router_split(w):
+    w = _c(w, np.float32)
+    hi = np.empty(w.shape, np.uint16)
+    lo = np.empty(w.shape, np.uint16)
+    lib().orc_router_split(_ptr(w), w.size, _ptr(hi), _ptr(lo))
+    return hi, lo
+
+
+def router_logits(x_bits, w, nthreads=None):
+    x_bits = _c(x_bits, np.uint16)
+    w = _c(w, np.float32)
+    T, H = x_bits.shape
+    E = w.shape[0]
+    out = np.empty((T, E), np.float64)
+    lib().orc_router_logits(_ptr(x_bits), _ptr(w), T, H, E, _ptr(out), nthreads or default_threads())
+    return out
+
+
+# ------------------------------------------------------------------ route / align
+def route(logits, k, bias=None, bias_rows=None):
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    b = None if bias is None else _c(bias, np.float32)
+    br = None if bias_rows is None else _c(bias_rows, np.uint8)
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    lib().orc_route(_ptr(logits), _ptr(b), _ptr(br), T, E, k, _ptr(ids), _ptr(w))
+    return ids, w
+
+
+def align(ids, E, shared):
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 2, np.int32)
+    slot_pair = np.empty(T * k, np.int32)
+    pair_slot = np.empty(T * k, np.int32)
+    lib().orc_align(_ptr(ids), T, E, k, int(shared), _ptr(counts), _ptr(offsets),
+                    _ptr(slot_pair), _ptr(pair_slot))
+    return counts, offsets, slot_pair, pair_slot
+
+
+# ------------------------------------------------------------------ fp8
+def quant_rows_fp8(x_bits):
+    x_bits = _c(x_bits, np.uint16)
+    rows, cols = x_bits.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 128), np.float32)
+    lib().orc_quant_rows_fp8(_ptr(x_bits), rows, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_blocks_fp8(w_bits):
+    """w_bits: [mats, rows, cols] (or [rows, cols]) bf16 bit patterns."""
+    w_bits = _c(w_bits, np.uint16)
+    squeeze = w_bits.ndim == 2
+    if squeeze:
+        w_bits = w_bits[None]
+    mats, rows, cols = w_bits.shape
+    q = np.empty(w_bits.shape, np.uint8)
+    s = np.empty((mats, rows // 128, cols // 128), np.float32)
+    lib().orc_quant_blocks_fp8(_ptr(w_bits), mats, rows, cols, _ptr(q), _ptr(s))
+    return (q[0], s[0]) if squeeze else (q, s)
+
+
+# ------------------------------------------------------------------ experts / layer
+def expert_bf16(x_bits, w1, w3, w2):
+    x_bits, w1, w3, w2 = (_c(a, np.uint16) for a in (x_bits, w1, w3, w2))
+    I, H = w1.shape
+    h = np.empty(I, np.float64)
+    y = np.empty(H, np.float64)
+    lib().orc_expert_bf16(_ptr(x_bits), _ptr(w1), _ptr(w3), _ptr(w2), H, I, _ptr(h), _ptr(y))
+    return h, y
+
+
+def expert_fp8(xq, xs, w1q, s1, w3q, s3, w2q, s2):
+    xq, w1q, w3q, w2q = (_c(a, np.uint8) for a in (xq, w1q, w3q, w2q))
+    xs, s1, s3, s2 = (_c(a, np.float32) for a in (xs, s1, s3, s2))
+    I, H = w1q.shape
+    h = np.empty(I, np.float64)
+    y = np.empty(H, np.float64)
+    lib().orc_expert_fp8(_ptr(xq), _ptr(xs), _ptr(w1q), _ptr(s1), _ptr(w3q), _ptr(s3),
+                         _ptr(w2q), _ptr(s2), H, I, _ptr(h), _ptr(y))
+    return h, y
+
+
+class Layer:
+    """Host copies of the expert weights.
+
+    bf16: ``Layer(w1, w3, w2, sw1=None, sw3=None, sw2=None)`` with uint16 arrays
+    w1, w3 [E, I, H], w2 [E, H, I] and the shared expert [I, H] / [H, I].
+    fp8: pass ``wtype=1`` plus uint8 codes and the fp32 block scales
+    s1, s3 [E, I/128, H/128], s2 [E, H/128, I/128] (and ss1/ss3/ss2).
+    """
+
+    def __init__(self, w1, w3, w2, sw1=None, sw3=None, sw2=None, wtype=0,
+                 s1=None, s3=None, s2=None, ss1=None, ss3=None, ss2=None):
+        dt = np.uint16 if wtype == 0 else np.uint8
+        self.arrays = {}
+        for name, a in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
+            self.arrays[name] = None if a is None else _c(a, dt)
+        for name, a in (("s1", s1), ("s3", s3), ("s2", s2), ("ss1", ss1), ("ss3", ss3), ("ss2", ss2)):
+            self.arrays[name] = None if a is None else _c(a, np.float32)
+        E, I, H = self.arrays["w1"].shape
+        self.E, self.I, self.H, self.wtype = E, I, H, wtype
+        self.has_shared = sw1 is not None
+        a = self.arrays
+        self.c = _Layer(wtype, E, H, I, int(self.has_shared),
+                        *(_ptr(a[n]) for n in ("w1", "w3", "w2", "s1", "s3", "s2",
+                                               "sw1", "sw3", "sw2", "ss1", "ss3", "ss2")))
+
+
+def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None):
+    """out[r] = sum_j w[t,j] FFN_{ids[t,j]}(x_t) + FFN_shared(x_t) for t = rows[r] (double)."""
+    dt = np.uint16 if layer.wtype == 0 else np.uint8
+    x = _c(x, dt)
+    xs = None if xs is None else _c(xs, np.float32)
+    ids = _c(ids, np.int32)
+    weights = _c(weights, np.float64)
+    rows = _c(rows, np.int64)
+    k = ids.shape[1]
+    out = np.empty((rows.size, layer.H), np.float64)
+    lib().orc_layer_rows(ctypes.byref(layer.c), _ptr(x), _ptr(xs), _ptr(ids), _ptr(weights), k,
+                         _ptr(rows), rows.size, _ptr(out), nthreads or default_threads())
+    return out
