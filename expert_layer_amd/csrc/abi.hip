@@ -1,0 +1,396 @@
+// C ABI of libmoe355: host-side validation and dispatch.  Every entry point
+// checks all of its arguments before it enqueues anything, so a refused call
+// launches nothing; none of the checks touches the device.
+#include <cstring>
+#include <mutex>
+
+#include "../../include/moe355.h"
+#include "common.hpp"
+
+namespace moe355 {
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace moe355
+
+using namespace moe355;
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;  // slot indices are int32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EDEVICE; }
+
+size_t round_up(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int check_route_shape(int64_t T, int E, int k) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_EINVAL;
+  if (E > 1024 || k > 32) return MOE_EUNSUPPORTED;
+  if (T * k >= kMaxRows) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_experts(const moe_experts_t* ex) {
+  if (ex == nullptr) return MOE_EINVAL;
+  if (ex->wtype != MOE_W_BF16 && ex->wtype != MOE_W_FP8) return MOE_EUNSUPPORTED;
+  if (ex->E <= 0 || ex->H <= 0 || ex->I <= 0) return MOE_EINVAL;
+  if (ex->has_shared != 0 && ex->has_shared != 1) return MOE_EINVAL;
+  if (ex->E > 1024 || ex->H % 128 != 0 || ex->I % 128 != 0) return MOE_EUNSUPPORTED;
+  if (!ex->w1 || !ex->w3 || !ex->w2) return MOE_EINVAL;
+  if (!aligned16(ex->w1) || !aligned16(ex->w3) || !aligned16(ex->w2)) return MOE_EINVAL;
+  if (ex->wtype == MOE_W_FP8 && (!ex->s1 || !ex->s3 || !ex->s2)) return MOE_EINVAL;
+  if (ex->has_shared) {
+    if (!ex->sw1 || !ex->sw3 || !ex->sw2) return MOE_EINVAL;
+    if (!aligned16(ex->sw1) || !aligned16(ex->sw3) || !aligned16(ex->sw2)) return MOE_EINVAL;
+    if (ex->wtype == MOE_W_FP8 && (!ex->ss1 || !ex->ss3 || !ex->ss2)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+int check_rows(const moe_experts_t* ex, int64_t T, int k) {
+  int st = check_route_shape(T, ex->E, k);
+  if (st != MOE_OK) return st;
+  if (T * k + (int64_t)ex->has_shared * T >= kMaxRows) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+GemmArgs gemm_args(const moe_experts_t* ex, int64_t T, int k, const int32_t* offsets, const int32_t* slot_pair) {
+  GemmArgs a;
+  a.w1 = ex->w1; a.w3 = ex->w3; a.w2 = ex->w2;
+  a.sw1 = ex->sw1; a.sw3 = ex->sw3; a.sw2 = ex->sw2;
+  a.s1 = ex->s1; a.s3 = ex->s3; a.s2 = ex->s2;
+  a.ss1 = ex->ss1; a.ss3 = ex->ss3; a.ss2 = ex->ss2;
+  a.E = ex->E; a.H = ex->H; a.I = ex->I; a.has_shared = ex->has_shared; a.k = k;
+  a.T = T;
+  a.offsets = offsets;
+  a.slot_pair = slot_pair;
+  return a;
+}
+
+}  // namespace
+
+#define MOE_GUARD_BEGIN try {
+#define MOE_GUARD_END \
+  }                   \
+  catch (...) {       \
+    return MOE_EDEVICE; \
+  }
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE355_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EDEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------ router
+int moe_router_split(const float* w, uint16_t* w_hi, uint16_t* w_lo, int E, int H, void* stream) {
+  MOE_GUARD_BEGIN
+  if (E < 0 || H < 0) return MOE_EINVAL;
+  const int64_t n = (int64_t)E * H;
+  if (n == 0) return MOE_OK;
+  if (!w || !w_hi || !w_lo) return MOE_EINVAL;
+  if (overlap(w_hi, n * 2, w_lo, n * 2) || overlap(w, n * 4, w_hi, n * 2) || overlap(w, n * 4, w_lo, n * 2))
+    return MOE_EINVAL;
+  return device_status(launch_router_split(w, w_hi, w_lo, n, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+int moe_router_gemm(const uint16_t* x, const uint16_t* w_hi, const uint16_t* w_lo, float* logits, int64_t T,
+                    int H, int E, void* stream) {
+  MOE_GUARD_BEGIN
+  if (T < 0 || H <= 0 || E <= 0) return MOE_EINVAL;
+  if (H % 128 != 0 || E > 1024) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_hi || !w_lo || !logits) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w_hi) || !aligned16(w_lo)) return MOE_EINVAL;
+  if (overlap(logits, (size_t)T * E * 4, x, (size_t)T * H * 2)) return MOE_EINVAL;
+  return device_status(launch_router_gemm(x, w_hi, w_lo, logits, T, H, E, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+// ------------------------------------------------------------------ route
+int moe_route(const float* logits, const float* bias, const uint8_t* bias_rows, int64_t T, int E, int k,
+              int32_t* topk_ids, float* topk_w, void* stream) {
+  MOE_GUARD_BEGIN
+  int st = check_route_shape(T, E, k);
+  if (st != MOE_OK) return st;
+  if (bias_rows != nullptr && bias == nullptr) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
+  if (overlap(topk_ids, (size_t)T * k * 4, topk_w, (size_t)T * k * 4)) return MOE_EINVAL;
+  return device_status(launch_route(logits, bias, bias_rows, T, E, k, topk_ids, topk_w, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+// ------------------------------------------------------------------ align
+size_t moe_align_workspace_bytes(int64_t T, int E, int k) {
+  if (T <= 0 || E <= 0 || k <= 0) return 0;
+  const int nb = align_blocks(T * k);
+  return nb <= 1 ? 0 : (size_t)nb * E * sizeof(int32_t);
+}
+
+int moe_align(const int32_t* topk_ids, int64_t T, int E, int k, int shared, int32_t* counts, int32_t* offsets,
+              int32_t* slot_pair, int32_t* pair_slot, void* ws, size_t ws_bytes, void* stream) {
+  MOE_GUARD_BEGIN
+  int st = check_route_shape(T, E, k);
+  if (st != MOE_OK) return st;
+  if (shared != 0 && shared != 1) return MOE_EINVAL;
+  if (T * k + shared * T >= kMaxRows) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !counts || !offsets || !slot_pair || !pair_slot) return MOE_EINVAL;
+  const size_t P4 = (size_t)T * k * 4;
+  const void* outs[4] = {counts, offsets, slot_pair, pair_slot};
+  const size_t sz[4] = {(size_t)E * 4, (size_t)(E + 2) * 4, P4, P4};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], sz[i], topk_ids, P4)) return MOE_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], sz[i], outs[j], sz[j])) return MOE_EINVAL;
+  }
+  const size_t need = moe_align_workspace_bytes(T, E, k);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_EWORKSPACE;
+  return device_status(launch_align(topk_ids, T, E, k, shared, counts, offsets, slot_pair, pair_slot,
+                                    static_cast<int32_t*>(ws), (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+// ------------------------------------------------------------------ fp8 helpers
+int moe_quant_rows_fp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s, void* stream) {
+  MOE_GUARD_BEGIN
+  if (rows < 0 || cols <= 0) return MOE_EINVAL;
+  if (cols % 128 != 0) return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !s) return MOE_EINVAL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u)) return MOE_EINVAL;
+  if (overlap(q, (size_t)rows * cols, s, (size_t)rows * (cols / 128) * 4)) return MOE_EINVAL;
+  return device_status(launch_quant_rows(x, rows, cols, q, s, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+int moe_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s,
+                         void* stream) {
+  MOE_GUARD_BEGIN
+  if (mats < 0 || rows <= 0 || cols <= 0) return MOE_EINVAL;
+  if (rows % 128 != 0 || cols % 128 != 0) return MOE_EUNSUPPORTED;
+  if (mats == 0) return MOE_OK;
+  if (!w || !q || !s) return MOE_EINVAL;
+  if (!aligned16(w) || (reinterpret_cast<uintptr_t>(q) & 7u)) return MOE_EINVAL;
+  if (mats * (rows / 128) * (cols / 128) >= kMaxRows) return MOE_EUNSUPPORTED;
+  return device_status(launch_quant_blocks(w, mats, rows, cols, q, s, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+// ------------------------------------------------------------------ grouped GEMMs
+size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k) {
+  (void)ex;
+  (void)T;
+  (void)k;
+  return 0;
+}
+
+int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const int32_t* offsets,
+               const int32_t* slot_pair, int64_t T, int k, void* h, float* hs, void* ws, size_t ws_bytes,
+               void* stream) {
+  MOE_GUARD_BEGIN
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_experts(ex);
+  if (st != MOE_OK) return st;
+  st = check_rows(ex, T, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !offsets || !slot_pair || !h) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(h)) return MOE_EINVAL;
+  const bool fp8 = ex->wtype == MOE_W_FP8;
+  if (fp8 && (!xs || !hs)) return MOE_EINVAL;
+  const int64_t R = T * k + ex->has_shared * T;
+  const size_t hbytes = (size_t)R * ex->I * (fp8 ? 1 : 2);
+  if (overlap(h, hbytes, x, (size_t)T * ex->H * (fp8 ? 1 : 2))) return MOE_EINVAL;
+  if (fp8 && overlap(hs, (size_t)R * (ex->I / 128) * 4, h, hbytes)) return MOE_EINVAL;
+  const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
+  hipStream_t s = (hipStream_t)stream;
+  if (fp8)
+    return device_status(launch_gemm13_fp8(a, static_cast<const uint8_t*>(x), xs, static_cast<uint8_t*>(h), hs, s));
+  return device_status(launch_gemm13_bf16(a, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), s));
+  MOE_GUARD_END
+}
+
+int moe_gemm2(const moe_experts_t* ex, const void* h, const float* hs, const int32_t* offsets, int64_t T, int k,
+              void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  MOE_GUARD_BEGIN
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_experts(ex);
+  if (st != MOE_OK) return st;
+  st = check_rows(ex, T, k);
+  if (st != MOE_OK) return st;
+  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!h || !offsets || !y) return MOE_EINVAL;
+  if (!aligned16(h) || !aligned16(y)) return MOE_EINVAL;
+  const bool fp8 = ex->wtype == MOE_W_FP8;
+  if (fp8 && !hs) return MOE_EINVAL;
+  const int64_t R = T * k + ex->has_shared * T;
+  if (overlap(y, (size_t)R * ex->H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2), h, (size_t)R * ex->I * (fp8 ? 1 : 2)))
+    return MOE_EINVAL;
+  const GemmArgs a = gemm_args(ex, T, k, offsets, nullptr);
+  hipStream_t s = (hipStream_t)stream;
+  if (fp8) return device_status(launch_gemm2_fp8(a, static_cast<const uint8_t*>(h), hs, y, y_dtype, s));
+  return device_status(launch_gemm2_bf16(a, static_cast<const uint16_t*>(h), y, y_dtype, s));
+  MOE_GUARD_END
+}
+
+// ------------------------------------------------------------------ combine
+int moe_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* topk_w, int64_t T, int k,
+                int H, int has_shared, uint16_t* out, void* stream) {
+  MOE_GUARD_BEGIN
+  if (T < 0 || k <= 0 || H <= 0) return MOE_EINVAL;
+  if (has_shared != 0 && has_shared != 1) return MOE_EINVAL;
+  if (k > 32 || H % 128 != 0) return MOE_EUNSUPPORTED;
+  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16) return MOE_EUNSUPPORTED;
+  if (T * k + has_shared * T >= kMaxRows) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y || !pair_slot || !topk_w || !out) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out)) return MOE_EINVAL;
+  const int64_t R = T * k + has_shared * T;
+  if (overlap(out, (size_t)T * H * 2, y, (size_t)R * H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2))) return MOE_EINVAL;
+  return device_status(launch_combine(y, y_dtype, pair_slot, topk_w, T, k, H, has_shared, out, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+// ------------------------------------------------------------------ whole chain
+namespace {
+
+struct FwdLayout {
+  size_t logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, xq, xs, h, hs, y, total;
+};
+
+FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype, bool router) {
+  FwdLayout L;
+  const int64_t P = T * k, R = P + ex->has_shared * T;
+  const bool fp8 = ex->wtype == MOE_W_FP8;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t at = off;
+    off += round_up(n);
+    return at;
+  };
+  L.logits = take(router ? (size_t)T * ex->E * 4 : 0);
+  L.ids = take((size_t)P * 4);
+  L.w = take((size_t)P * 4);
+  L.counts = take((size_t)ex->E * 4);
+  L.offsets = take((size_t)(ex->E + 2) * 4);
+  L.slot_pair = take((size_t)P * 4);
+  L.pair_slot = take((size_t)P * 4);
+  L.align_ws = take(moe_align_workspace_bytes(T, ex->E, k));
+  L.xq = take(fp8 ? (size_t)T * ex->H : 0);
+  L.xs = take(fp8 ? (size_t)T * (ex->H / 128) * 4 : 0);
+  L.h = take((size_t)R * ex->I * (fp8 ? 1 : 2));
+  L.hs = take(fp8 ? (size_t)R * (ex->I / 128) * 4 : 0);
+  L.y = take((size_t)R * ex->H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t moe_forward_workspace_bytes(const moe_experts_t* ex, int64_t T, int k, int y_dtype) {
+  if (check_experts(ex) != MOE_OK || check_rows(ex, T, k) != MOE_OK) return 0;
+  return forward_layout(ex, T, k, y_dtype, true).total;
+}
+
+int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, void* stream) {
+  MOE_GUARD_BEGIN
+  if (!args) return MOE_EINVAL;
+  int st = check_experts(ex);
+  if (st != MOE_OK) return st;
+  const int64_t T = args->T;
+  const int k = args->k;
+  st = check_rows(ex, T, k);
+  if (st != MOE_OK) return st;
+  if (args->y_dtype != MOE_DTYPE_F32 && args->y_dtype != MOE_DTYPE_BF16) return MOE_EUNSUPPORTED;
+  const bool router = args->logits == nullptr;
+  if (router && (!args->router_hi || !args->router_lo)) return MOE_EINVAL;
+  if (args->bias_rows && !args->bias) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!args->x || !args->out) return MOE_EINVAL;
+  if (!aligned16(args->x) || !aligned16(args->out)) return MOE_EINVAL;
+  if (router && (!aligned16(args->router_hi) || !aligned16(args->router_lo))) return MOE_EINVAL;
+  // the workspace always has room for the logits, matching moe_forward_workspace_bytes
+  const FwdLayout L = forward_layout(ex, T, k, args->y_dtype, true);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (overlap(ws, L.total, args->out, (size_t)T * ex->H * 2) || overlap(ws, L.total, args->x, (size_t)T * ex->H * 2))
+    return MOE_EINVAL;
+
+  char* base = static_cast<char*>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  const int E = ex->E;
+  const bool fp8 = ex->wtype == MOE_W_FP8;
+  float* logits = router ? reinterpret_cast<float*>(base + L.logits) : nullptr;
+  int32_t* ids = args->topk_ids ? args->topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
+  float* w = args->topk_w ? args->topk_w : reinterpret_cast<float*>(base + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* slot_pair = reinterpret_cast<int32_t*>(base + L.slot_pair);
+  int32_t* pair_slot = reinterpret_cast<int32_t*>(base + L.pair_slot);
+  int32_t* align_ws = reinterpret_cast<int32_t*>(base + L.align_ws);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + L.xq);
+  float* xs = reinterpret_cast<float*>(base + L.xs);
+  void* h = base + L.h;
+  float* hs = reinterpret_cast<float*>(base + L.hs);
+  void* y = base + L.y;
+
+  hipError_t e;
+  if (router) {
+    e = launch_router_gemm(args->x, args->router_hi, args->router_lo, logits, T, ex->H, E, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+  }
+  e = launch_route(router ? logits : args->logits, args->bias, args->bias_rows, T, E, k, ids, w, s);
+  if (e != hipSuccess) return MOE_EDEVICE;
+  e = launch_align(ids, T, E, k, ex->has_shared, counts, offsets, slot_pair, pair_slot, align_ws, s);
+  if (e != hipSuccess) return MOE_EDEVICE;
+  const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
+  if (fp8) {
+    e = launch_quant_rows(args->x, T, ex->H, xq, xs, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm13_fp8(a, xq, xs, static_cast<uint8_t*>(h), hs, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm2_fp8(a, static_cast<const uint8_t*>(h), hs, y, args->y_dtype, s);
+  } else {
+    e = launch_gemm13_bf16(a, args->x, static_cast<uint16_t*>(h), s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm2_bf16(a, static_cast<const uint16_t*>(h), y, args->y_dtype, s);
+  }
+  if (e != hipSuccess) return MOE_EDEVICE;
+  e = launch_combine(y, args->y_dtype, pair_slot, w, T, k, ex->H, ex->has_shared, args->out, s);
+  return device_status(e);
+  MOE_GUARD_END
+}
+
+}  // extern "C"

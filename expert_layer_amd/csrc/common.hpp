@@ -1,0 +1,90 @@
+// Device helpers and internal launcher declarations for libmoe355 (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe355 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two fp32 values -> two OCP E4M3FN codes (RNE, saturated to +-448) packed in
+// the low 16 bits.  The hardware conversion rounds to nearest even; the clamp
+// makes the saturation explicit.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_max16(float v) {
+  // max over the 16 lanes that share (lane / 16)
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+// ------------------------------------------------------------------ launchers
+// All launchers enqueue on `s` and return hipGetLastError().  Shapes have been
+// validated by the ABI layer.
+hipError_t launch_route(const float* logits, const float* bias, const uint8_t* bias_rows, int64_t T,
+                        int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+int align_blocks(int64_t P);
+hipError_t launch_align(const int32_t* ids, int64_t T, int E, int k, int shared, int32_t* counts,
+                        int32_t* offsets, int32_t* slot_pair, int32_t* pair_slot, int32_t* ws,
+                        hipStream_t s);
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
+                             hipStream_t s);
+hipError_t launch_quant_blocks(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q,
+                               float* sc, hipStream_t s);
+
+hipError_t launch_router_split(const float* w, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* hi, const uint16_t* lo, float* logits,
+                              int64_t T, int H, int E, hipStream_t s);
+
+struct GemmArgs {
+  // expert weights (routed [E,...] and shared)
+  const void *w1, *w3, *w2, *sw1, *sw3, *sw2;
+  const float *s1, *s3, *s2, *ss1, *ss3, *ss2;
+  int E, H, I, has_shared, k;
+  int64_t T;
+  const int32_t* offsets;    // [E+2]
+  const int32_t* slot_pair;  // [P]
+};
+
+hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
+hipError_t launch_gemm2_bf16(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm13_fp8(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq,
+                             float* hs, hipStream_t s);
+hipError_t launch_gemm2_fp8(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
+                            hipStream_t s);
+
+hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
+                          int k, int H, int has_shared, uint16_t* out, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cus();
+
+}  // namespace moe355

@@ -1,0 +1,109 @@
+// FP8 quantisers (OCP E4M3FN, nearest-even, saturating).
+//  * rows:   per row, per group of 128 columns (activations before the gathered
+//            Gate-Up GEMM);
+//  * blocks: per 128x128 block of a weight matrix (the FP8 blockwise 128x128
+//            checkpoint format of the PR #54160 report, implementation item 4).
+// Scale = amax / 448 with a correctly rounded fp32 division (1 when amax is 0);
+// code = e4m3(fp32(v / scale)).
+#include "common.hpp"
+
+namespace moe355 {
+
+namespace {
+
+// 16 lanes per 128-column group, 8 columns (16 bytes of bf16) per lane.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                         int cols, uint8_t* __restrict__ q,
+                                                         float* __restrict__ sc) {
+  const int groups = cols / 128;
+  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int64_t ngroups = rows * groups;
+  const bool live = g < ngroups;
+  const int64_t r = live ? g / groups : 0;
+  const int c0 = live ? (int)(g % groups) * 128 + sub * 8 : 0;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) raw = *reinterpret_cast<const uint4*>(x + r * cols + c0);
+  float v[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max16(amax);
+  const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  uint32_t lo = f32x2_to_e4m3(__fdiv_rn(v[0], s), __fdiv_rn(v[1], s)) |
+                (f32x2_to_e4m3(__fdiv_rn(v[2], s), __fdiv_rn(v[3], s)) << 16);
+  uint32_t hi = f32x2_to_e4m3(__fdiv_rn(v[4], s), __fdiv_rn(v[5], s)) |
+                (f32x2_to_e4m3(__fdiv_rn(v[6], s), __fdiv_rn(v[7], s)) << 16);
+  if (live) {
+    *reinterpret_cast<uint2*>(q + r * cols + c0) = make_uint2(lo, hi);
+    if (sub == 0) sc[g] = s;
+  }
+}
+
+// One workgroup (256 threads) per 128x128 block: 64 elements per thread.
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ w, int rows,
+                                                           int cols, uint8_t* __restrict__ q,
+                                                           float* __restrict__ sc) {
+  __shared__ float red[4];
+  const int rb = rows / 128, cb = cols / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t m = blk / ((int64_t)rb * cb);
+  const int bi = (int)((blk / cb) % rb), bj = (int)(blk % cb);
+  // pass p covers rows p*16 .. p*16+15; thread (tr, tc) takes 8 columns of row p*16+tr
+  const int tr = threadIdx.x >> 4;        // 0..15
+  const int tc = (threadIdx.x & 15) * 8;  // 0..120
+  const uint16_t* base = w + (m * rows + (int64_t)bi * 128) * cols + (int64_t)bj * 128;
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + (int64_t)(p * 16 + tr) * cols + tc);
+    const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[p][2 * i] = bf16_to_f32(u[i] & 0xFFFFu);
+      v[p][2 * i + 1] = bf16_to_f32(u[i] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(v[p][2 * i]), fabsf(v[p][2 * i + 1])));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  uint8_t* qb = q + (m * rows + (int64_t)bi * 128) * cols + (int64_t)bj * 128;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    uint32_t lo = f32x2_to_e4m3(__fdiv_rn(v[p][0], s), __fdiv_rn(v[p][1], s)) |
+                  (f32x2_to_e4m3(__fdiv_rn(v[p][2], s), __fdiv_rn(v[p][3], s)) << 16);
+    uint32_t hi = f32x2_to_e4m3(__fdiv_rn(v[p][4], s), __fdiv_rn(v[p][5], s)) |
+                  (f32x2_to_e4m3(__fdiv_rn(v[p][6], s), __fdiv_rn(v[p][7], s)) << 16);
+    *reinterpret_cast<uint2*>(qb + (int64_t)(p * 16 + tr) * cols + tc) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) sc[blk] = s;
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
+                             hipStream_t s) {
+  const int64_t groups = rows * (cols / 128);
+  quant_rows_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, s>>>(x, rows, cols, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_blocks(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* sc,
+                               hipStream_t s) {
+  const int64_t nblk = mats * (rows / 128) * (cols / 128);
+  quant_blocks_kernel<<<(unsigned)nblk, 256, 0, s>>>(w, rows, cols, q, sc);
+  return hipGetLastError();
+}
+
+}  // namespace moe355

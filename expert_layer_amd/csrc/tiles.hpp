@@ -1,0 +1,76 @@
+// Persistent tile scheduler for the grouped expert GEMMs.
+//
+// Groups are the E routed experts plus (optionally) the shared expert as
+// group E; group g owns slots [offsets[g], offsets[g+1]).  A group is cut into
+// row chunks of at most `chunk_rows` rows; an item is (chunk, column tile).
+// Every workgroup rebuilds the chunk prefix over groups in LDS from
+// `offsets` (a few hundred integers), so the grid never depends on the
+// routing result known only on the device: the grid is sized to fill the
+// chip and each wave strides over the item list.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe355 {
+
+constexpr int kMaxGroups = 1025;
+
+struct ChunkTable {
+  int prefix[kMaxGroups + 1];  // prefix[g] = chunks in groups < g
+  int wsum[16];
+};
+
+// Build the chunk prefix for G groups.  Must be called by all threads of the
+// workgroup (contains barriers).  Returns the total chunk count.
+__device__ inline int build_chunks(ChunkTable& tab, const int32_t* __restrict__ offsets, int G,
+                                   int chunk_rows) {
+  const int nthreads = blockDim.x;
+  const int per = (G + nthreads - 1) / nthreads;
+  const int g0 = threadIdx.x * per;
+  int local = 0;
+  for (int g = g0; g < g0 + per && g < G; ++g) {
+    const int rows = offsets[g + 1] - offsets[g];
+    local += (rows + chunk_rows - 1) / chunk_rows;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int v = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int n = __shfl_up(v, off);
+    if (lane >= off) v += n;
+  }
+  if (lane == 63) tab.wsum[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < (nthreads + 63) / 64; ++w) {
+      const int c = tab.wsum[w];
+      tab.wsum[w] = run;
+      run += c;
+    }
+    tab.prefix[G] = run;
+  }
+  __syncthreads();
+  int run = v - local + tab.wsum[wave];
+  for (int g = g0; g < g0 + per && g < G; ++g) {
+    tab.prefix[g] = run;
+    const int rows = offsets[g + 1] - offsets[g];
+    run += (rows + chunk_rows - 1) / chunk_rows;
+  }
+  __syncthreads();
+  return tab.prefix[G];
+}
+
+// Group owning chunk c: the last g with prefix[g] <= c (empty groups skipped).
+__device__ inline int chunk_group(const ChunkTable& tab, int G, int c) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.prefix[mid] <= c)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace moe355

@@ -1,0 +1,213 @@
+/*
+ * libmoe355 -- fused Mixture-of-Experts layer forward for AMD Instinct MI355X
+ * (CDNA4, gfx950).  C ABI.
+ *
+ * The method: the five-stage FusedMoE chain of Tencent's HPC-Ops
+ * ("HPC-Ops" overview page, sections "Main functions" and "Technical
+ * principles"): routing index -> Gate-Up GEMM -> activation quantisation ->
+ * Down GEMM -> top-k weighted combine, with the split-BF16 router GEMM as an
+ * optional front end, for a Hy4-preview style block (PR #54160 report,
+ * "Features and motivation": 256 routed experts, top-8, plus one shared
+ * expert).
+ *
+ * Conventions for every call
+ *  - Array pointers are DEVICE pointers unless stated otherwise; arrays are
+ *    row-major and contiguous.  bf16 is carried as uint16_t bit patterns,
+ *    FP8 as uint8_t codes in OCP E4M3FN (max 448, no infinities).
+ *  - The caller allocates and owns every buffer, including workspaces whose
+ *    size the *_workspace_bytes queries return.  The library allocates no
+ *    device memory and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Calls are asynchronous on that stream.
+ *  - Every call validates its arguments on the host before enqueuing
+ *    anything and returns a status: on error nothing is launched.  A call
+ *    with T == 0 (or zero rows) returns MOE_OK and enqueues nothing.  No C++
+ *    exception crosses the ABI.  Shapes outside the compiled envelope are
+ *    refused with MOE_EUNSUPPORTED; there is no silent fallback path.
+ *  - Stateless and re-entrant.  For fixed inputs and shapes every output is
+ *    bitwise identical from run to run (no floating-point atomics).
+ *
+ * Symbols used below: T tokens, H hidden size, E routed experts, k experts
+ * per token, I expert intermediate size, S in {0,1} shared experts.
+ * P = T*k routed (token, rank) pairs, pair index p = t*k + j.
+ * R = P + S*T rows in "slot space": slots [0,P) are grouped by expert
+ * (group e owns slots [offsets[e], offsets[e+1])), slots [P, P+T) belong to
+ * the shared expert (group E) in token order.
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE355_ABI_VERSION 1
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* NULL required pointer, negative size, k > E, overlapping outputs */
+  MOE_EUNSUPPORTED = 2,  /* outside the envelope: H or I not a multiple of 128, E > 1024,
+                            k > 32, R >= 2^31, unknown dtype */
+  MOE_EWORKSPACE = 3,    /* workspace NULL or smaller than the query returned */
+  MOE_EDEVICE = 4        /* a HIP error reported right after a launch */
+};
+
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };  /* y_dtype */
+enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1 };          /* moe_experts_t.wtype */
+
+int moe_abi_version(void);
+const char* moe_status_string(int status);
+
+/* ------------------------------------------------------------------ router
+ * Split-BF16 router (HPC-Ops page, "Router GEMM" in main functions and
+ * technical principles): fp32 router weights are split offline into a high
+ * bf16 part and a residual bf16 part with scale 1/256, and the logits are two
+ * bf16 GEMMs combined linearly in one kernel with one FMA in the epilogue.
+ *
+ * moe_router_split (offline):  w fp32 [E,H] -> w_hi, w_lo bf16 [E,H] with
+ *   w_hi = bf16_rne(w), w_lo = bf16_rne((w - w_hi) * 256).
+ * moe_router_gemm:  x bf16 [T,H], w_hi, w_lo [E,H] -> logits fp32 [T,E],
+ *   logits = fma(x.w_lo^T, 1/256, x.w_hi^T), both products accumulated in
+ *   fp32 on the bf16 matrix cores; x is read once.  H % 128 == 0, E <= 1024.
+ */
+int moe_router_split(const float* w, uint16_t* w_hi, uint16_t* w_lo, int E, int H, void* stream);
+int moe_router_gemm(const uint16_t* x, const uint16_t* w_hi, const uint16_t* w_lo, float* logits,
+                    int64_t T, int H, int E, void* stream);
+
+/* ------------------------------------------------------------------ stage 1: route
+ * Routing index (HPC-Ops page, FusedMoE stage 1).  Per token t:
+ *   l'[e] = logits[t,e] + bias[e] (fp32 add) if bias != NULL and
+ *           (bias_rows == NULL or bias_rows[t] != 0), else logits[t,e];
+ *   topk_ids[t, 0..k-1] = the k experts with the largest l', ordered by
+ *           value descending, ties to the lower expert id;
+ *   topk_w[t, j] = exp(l'_j - l'_0) / sum_i exp(l'_i - l'_0)  (softmax over
+ *           the k selected values; no capacity limit, nothing dropped).
+ * logits fp32 [T,E]; bias fp32 [E] or NULL; bias_rows uint8 [T] or NULL;
+ * topk_ids int32 [T,k]; topk_w fp32 [T,k].  1 <= k <= min(E, 32), E <= 1024.
+ */
+int moe_route(const float* logits, const float* bias, const uint8_t* bias_rows, int64_t T, int E,
+              int k, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------ stage 1b: align
+ * Per-expert histogram in LDS, exclusive prefix sum, and a contiguous output
+ * interval per expert (HPC-Ops page, technical principles: FusedMoE routing
+ * stage).  Slots inside an interval follow ascending pair index, hence
+ * ascending token (a token's k experts are distinct).
+ *   counts int32 [E]; offsets int32 [E+2]: offsets[e] = sum_{e'<e} counts[e'],
+ *   offsets[E] = P, offsets[E+1] = P + shared*T;
+ *   slot_pair int32 [P]: pair stored in slot s; pair_slot int32 [P]: inverse.
+ * ws: device scratch of moe_align_workspace_bytes(T, E, k) bytes (may be 0;
+ * ws may then be NULL).  topk_ids must hold valid ids in [0,E) with k
+ * distinct ids per token (the output of moe_route); other input is undefined
+ * behaviour.
+ */
+size_t moe_align_workspace_bytes(int64_t T, int E, int k);
+int moe_align(const int32_t* topk_ids, int64_t T, int E, int k, int shared, int32_t* counts,
+              int32_t* offsets, int32_t* slot_pair, int32_t* pair_slot, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* ------------------------------------------------------------------ FP8 helpers
+ * OCP E4M3FN, round to nearest even, saturating at +-448.  Scale of a
+ * group/block = amax / 448 in fp32 (1 when amax == 0); code = e4m3(fp32(v / s)).
+ * moe_quant_rows_fp8: activations, per row per group of 128 columns
+ *   (x bf16 [rows,cols] -> q [rows,cols], s fp32 [rows, cols/128]).
+ * moe_quant_blocks_fp8 (offline): weights with 128x128 block scales, the
+ *   checkpoint format named in the PR #54160 report (implementation item 4)
+ *   (w bf16 [mats,rows,cols] -> q [mats,rows,cols], s fp32 [mats, rows/128, cols/128]).
+ * rows/cols of a block-quantised matrix and cols of a row-quantised one must be
+ * multiples of 128.
+ */
+int moe_quant_rows_fp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* s, void* stream);
+int moe_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s,
+                         void* stream);
+
+/* ------------------------------------------------------------------ experts
+ * SwiGLU experts: h = SiLU(x.w1^T) * (x.w3^T) (w1 = gate, w3 = up),
+ * y = h.w2^T.  Routed: w1, w3 [E,I,H], w2 [E,H,I].  Shared expert (if
+ * has_shared): sw1, sw3 [I,H], sw2 [H,I].  wtype MOE_W_BF16: bf16 weights,
+ * scale pointers ignored.  wtype MOE_W_FP8: e4m3 codes plus fp32 128x128 block
+ * scales s1, s3 [E,I/128,H/128], s2 [E,H/128,I/128], ss1, ss3 [I/128,H/128],
+ * ss2 [H/128,I/128].  The struct itself is host memory; the pointers in it are
+ * device pointers.
+ */
+typedef struct moe_experts_t {
+  int wtype;
+  int E, H, I, has_shared;
+  const void *w1, *w3, *w2;
+  const float *s1, *s3, *s2;
+  const void *sw1, *sw3, *sw2;
+  const float *ss1, *ss3, *ss2;
+} moe_experts_t;
+
+/* ------------------------------------------------------------------ stages 2-3: Gate-Up GEMM
+ * Grouped Gate-Up GEMM with SwiGLU (and, for FP8, the activation
+ * requantisation stage fused into its epilogue).  For every slot s of group
+ * g (HPC-Ops page, technical principles: the Gate-Up GEMM reads the input
+ * directly through the routing index, with no separate gather copy):
+ *   t = slot_pair[s] / k for routed slots, t = s - P for shared slots;
+ *   h[s] = SiLU(x[t].w1[g]^T) * (x[t].w3[g]^T), fp32 accumulation.
+ * bf16: x bf16 [T,H], xs NULL, h bf16 [R,I], hs NULL.
+ * fp8:  x e4m3 [T,H] with xs fp32 [T,H/128] (moe_quant_rows_fp8); partial
+ *   sums over each 128-wide K block are scaled by xs[t,kb] * s[g,n/128,kb];
+ *   h is requantised per row per 128 columns into h e4m3 [R,I] and hs fp32
+ *   [R,I/128] with the same rule as moe_quant_rows_fp8.
+ * offsets, slot_pair: from moe_align.  ws: moe_gemm_workspace_bytes bytes.
+ */
+size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k);
+int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const int32_t* offsets,
+               const int32_t* slot_pair, int64_t T, int k, void* h, float* hs, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ stage 4: Down GEMM
+ * y[s] = h[s].w2[g]^T for every slot s of group g (fp32 accumulation; fp8
+ * partial sums per 128-wide K block scaled by hs[s,kb] * s2[g,n/128,kb]).
+ * y is fp32 (y_dtype MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16), [R,H].
+ */
+int moe_gemm2(const moe_experts_t* ex, const void* h, const float* hs, const int32_t* offsets,
+              int64_t T, int k, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ stage 5: combine
+ * Top-k weighted combine (HPC-Ops page, FusedMoE stage 5):
+ *   out[t] = sum_{j=0..k-1} topk_w[t,j] * y[pair_slot[t*k+j]] + has_shared * y[P+t],
+ * summed in that fixed order in fp32 and rounded once to bf16 (no atomics).
+ * y [R,H] fp32 or bf16; out bf16 [T,H].
+ */
+int moe_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* topk_w, int64_t T,
+                int k, int H, int has_shared, uint16_t* out, void* stream);
+
+/* ------------------------------------------------------------------ the whole chain
+ * Convenience entry point that enqueues the chain on one stream:
+ * [router_gemm] -> route -> align -> [quant_rows_fp8] -> gemm13 -> gemm2 -> combine.
+ * Either logits (fp32 [T,E]) or the split router weights (router_hi/lo bf16
+ * [E,H]) must be given.  x bf16 [T,H]; out bf16 [T,H].  Every intermediate
+ * lives in the caller's workspace (moe_forward_workspace_bytes bytes); the
+ * layout of the workspace is private.  topk_ids/topk_w may be NULL; if given
+ * ([T,k] each) the routing result is also copied there.
+ */
+typedef struct moe_forward_args_t {
+  int64_t T;
+  int k;
+  int y_dtype;
+  const uint16_t* x;
+  const float* logits;
+  const uint16_t* router_hi;
+  const uint16_t* router_lo;
+  const float* bias;
+  const uint8_t* bias_rows;
+  uint16_t* out;
+  int32_t* topk_ids;
+  float* topk_w;
+} moe_forward_args_t;
+
+size_t moe_forward_workspace_bytes(const moe_experts_t* ex, int64_t T, int k, int y_dtype);
+int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE355_H */

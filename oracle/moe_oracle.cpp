@@ -277,11 +277,24 @@ void orc_expert_bf16(const uint16_t* x, const uint16_t* w1, const uint16_t* w3, 
 
 // Blockwise-scaled fp8 dot product of one activation row with one weight row:
 // sum over 128-wide K blocks of (xs[kb] * ws[kb]) * sum_k dec(xq[k]) * dec(wq[k]).
+// Value of every E4M3 code, filled once from e4m3_value (a cache, not a
+// different definition).
+static const double* e4m3_table() {
+  static double table[256];
+  static bool ready = [] {
+    for (int c = 0; c < 256; ++c) table[c] = e4m3_value(static_cast<uint8_t>(c));
+    return true;
+  }();
+  (void)ready;
+  return table;
+}
+
 static double fp8_dot(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, int K) {
+  const double* dec = e4m3_table();
   double acc = 0.0;
   for (int kb = 0; kb < K / 128; ++kb) {
     double part = 0.0;
-    for (int i = 0; i < 128; ++i) part += e4m3_value(xq[kb * 128 + i]) * e4m3_value(wq[kb * 128 + i]);
+    for (int i = 0; i < 128; ++i) part += dec[xq[kb * 128 + i]] * dec[wq[kb * 128 + i]];
     acc += static_cast<double>(xs[kb]) * static_cast<double>(ws[kb]) * part;
   }
   return acc;
@@ -341,40 +354,120 @@ struct orc_layer {
 // bf16 path: x is bf16 [T,H] and xs is NULL.  fp8 path: x is the e4m3 code
 // array [T,H] and xs [T,H/128] its scales (from orc_quant_rows_fp8).
 // ids / weights are the route output [T,k].  out: [nrows, H] double.
+//
+// The arithmetic per (token, expert) is exactly orc_expert_bf16 /
+// orc_expert_fp8; the loops only run expert by expert so that each expert's
+// weight rows are read once for all the checked tokens that use it.
 void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const int32_t* ids,
                     const double* weights, int k, const int64_t* rows, int64_t nrows, double* out,
                     int nthreads) {
-  const int H = L->H, I = L->I;
+  const int H = L->H, I = L->I, E = L->E;
+  const int hb = H / 128, ib = I / 128;
   const int64_t mat = (int64_t)I * H;
-  const int64_t blk = (int64_t)(I / 128) * (H / 128);
+  const int64_t blk = (int64_t)ib * hb;
+  const int per_row = k + (L->has_shared ? 1 : 0);
+  const int64_t npairs = nrows * per_row;
+  const bool fp8 = L->wtype != 0;
+
+  // pair q = r * per_row + j: token rows[r], expert ids[t,j] (j < k) or the
+  // shared expert (group E, j == k)
+  std::vector<std::vector<int64_t>> members(E + 1);
+  for (int64_t r = 0; r < nrows; ++r)
+    for (int j = 0; j < per_row; ++j) {
+      const int g = j == k ? E : ids[rows[r] * k + j];
+      members[g].push_back(r * per_row + j);
+    }
+  auto token_of = [&](int64_t q) { return rows[q / per_row]; };
+
+  std::vector<double> hbuf(npairs * (int64_t)I);   // h per pair (double; fp8: fp32-rounded)
+  std::vector<uint8_t> hq(fp8 ? npairs * (int64_t)I : 0);
+  std::vector<float> hs(fp8 ? npairs * (int64_t)ib : 0);
+  std::vector<double> ybuf(npairs * (int64_t)H);
+
+  // phase 1: h = SiLU(x.w1^T) * (x.w3^T) for every pair, task = (group, 128 rows of w1/w3)
+  const int nt1 = I / 128;
+  parallel_for((int64_t)(E + 1) * nt1, nthreads, [&](int64_t task) {
+    const int g = (int)(task / nt1), n0 = (int)(task % nt1) * 128;
+    if (members[g].empty()) return;
+    const bool sh = g == E;
+    std::vector<double> xv(H);
+    for (int64_t q : members[g]) {
+      const int64_t t = token_of(q);
+      for (int n = n0; n < n0 + 128; ++n) {
+        double gv, uv;
+        if (!fp8) {
+          const uint16_t* xr = static_cast<const uint16_t*>(x) + t * H;
+          const uint16_t* w1 = (sh ? static_cast<const uint16_t*>(L->sw1) : static_cast<const uint16_t*>(L->w1) + g * mat) + (int64_t)n * H;
+          const uint16_t* w3 = (sh ? static_cast<const uint16_t*>(L->sw3) : static_cast<const uint16_t*>(L->w3) + g * mat) + (int64_t)n * H;
+          gv = 0.0;
+          uv = 0.0;
+          for (int i = 0; i < H; ++i) {
+            const double xi = bf16_value(xr[i]);
+            gv += xi * bf16_value(w1[i]);
+            uv += xi * bf16_value(w3[i]);
+          }
+          hbuf[q * I + n] = silu(gv) * uv;
+        } else {
+          const uint8_t* xr = static_cast<const uint8_t*>(x) + t * H;
+          const float* xsr = xs + t * hb;
+          const uint8_t* w1 = (sh ? static_cast<const uint8_t*>(L->sw1) : static_cast<const uint8_t*>(L->w1) + g * mat) + (int64_t)n * H;
+          const uint8_t* w3 = (sh ? static_cast<const uint8_t*>(L->sw3) : static_cast<const uint8_t*>(L->w3) + g * mat) + (int64_t)n * H;
+          const float* s1 = (sh ? L->ss1 : L->s1 + g * blk) + (n / 128) * hb;
+          const float* s3 = (sh ? L->ss3 : L->s3 + g * blk) + (n / 128) * hb;
+          gv = fp8_dot(xr, xsr, w1, s1, H);
+          uv = fp8_dot(xr, xsr, w3, s3, H);
+          hbuf[q * I + n] = static_cast<float>(silu(gv) * uv);
+        }
+      }
+    }
+  });
+
+  // fp8: requantise each pair's h per 128 columns (scale amax/448)
+  if (fp8) {
+    parallel_for(npairs, nthreads, [&](int64_t q) {
+      for (int gi = 0; gi < ib; ++gi) {
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i) amax = std::max(amax, std::fabs(static_cast<float>(hbuf[q * I + gi * 128 + i])));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        hs[q * ib + gi] = sc;
+        for (int i = 0; i < 128; ++i)
+          hq[q * I + gi * 128 + i] = e4m3_code(static_cast<float>(hbuf[q * I + gi * 128 + i]) / sc);
+      }
+    });
+  }
+
+  // phase 2: y = h.w2^T for every pair, task = (group, 128 rows of w2)
+  const int nt2 = H / 128;
+  parallel_for((int64_t)(E + 1) * nt2, nthreads, [&](int64_t task) {
+    const int g = (int)(task / nt2), m0 = (int)(task % nt2) * 128;
+    if (members[g].empty()) return;
+    const bool sh = g == E;
+    for (int64_t q : members[g]) {
+      for (int m = m0; m < m0 + 128; ++m) {
+        double acc;
+        if (!fp8) {
+          const uint16_t* w2 = (sh ? static_cast<const uint16_t*>(L->sw2) : static_cast<const uint16_t*>(L->w2) + g * mat) + (int64_t)m * I;
+          acc = 0.0;
+          for (int n = 0; n < I; ++n) acc += hbuf[q * I + n] * bf16_value(w2[n]);
+        } else {
+          const uint8_t* w2 = (sh ? static_cast<const uint8_t*>(L->sw2) : static_cast<const uint8_t*>(L->w2) + g * mat) + (int64_t)m * I;
+          const float* s2 = (sh ? L->ss2 : L->s2 + g * blk) + (m / 128) * ib;
+          acc = fp8_dot(hq.data() + q * I, hs.data() + q * ib, w2, s2, I);
+        }
+        ybuf[q * H + m] = acc;
+      }
+    }
+  });
+
+  // combine in fixed order: routed ranks j = 0..k-1, then the shared expert
   parallel_for(nrows, nthreads, [&](int64_t r) {
-    int64_t t = rows[r];
-    std::vector<double> y(H);
+    const int64_t t = rows[r];
     double* o = out + r * H;
     for (int m = 0; m < H; ++m) o[m] = 0.0;
-    int nexp = k + (L->has_shared ? 1 : 0);
-    for (int j = 0; j < nexp; ++j) {
-      bool shared = j == k;
-      int e = shared ? 0 : ids[t * k + j];
-      double wt = shared ? 1.0 : weights[t * k + j];
-      if (L->wtype == 0) {
-        const uint16_t* xr = static_cast<const uint16_t*>(x) + t * H;
-        const uint16_t* w1 = shared ? static_cast<const uint16_t*>(L->sw1) : static_cast<const uint16_t*>(L->w1) + e * mat;
-        const uint16_t* w3 = shared ? static_cast<const uint16_t*>(L->sw3) : static_cast<const uint16_t*>(L->w3) + e * mat;
-        const uint16_t* w2 = shared ? static_cast<const uint16_t*>(L->sw2) : static_cast<const uint16_t*>(L->w2) + e * mat;
-        orc_expert_bf16(xr, w1, w3, w2, H, I, nullptr, y.data());
-      } else {
-        const uint8_t* xr = static_cast<const uint8_t*>(x) + t * H;
-        const float* xsr = xs + t * (H / 128);
-        const uint8_t* w1 = shared ? static_cast<const uint8_t*>(L->sw1) : static_cast<const uint8_t*>(L->w1) + e * mat;
-        const uint8_t* w3 = shared ? static_cast<const uint8_t*>(L->sw3) : static_cast<const uint8_t*>(L->w3) + e * mat;
-        const uint8_t* w2 = shared ? static_cast<const uint8_t*>(L->sw2) : static_cast<const uint8_t*>(L->w2) + e * mat;
-        const float* s1 = shared ? L->ss1 : L->s1 + e * blk;
-        const float* s3 = shared ? L->ss3 : L->s3 + e * blk;
-        const float* s2 = shared ? L->ss2 : L->s2 + e * blk;
-        orc_expert_fp8(xr, xsr, w1, s1, w3, s3, w2, s2, H, I, nullptr, y.data());
-      }
-      for (int m = 0; m < H; ++m) o[m] += wt * y[m];
+    for (int j = 0; j < per_row; ++j) {
+      const int64_t q = r * per_row + j;
+      const double wt = j == k ? 1.0 : weights[t * k + j];
+      for (int m = 0; m < H; ++m) o[m] += wt * ybuf[q * H + m];
     }
   });
 }

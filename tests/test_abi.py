@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/moe355.h, and refuses bad arguments with the documented
+status codes before anything is launched (fake, never-dereferenced device
+pointers are enough because validation is host-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_layer_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe355.h")
+
+A = 0x100000      # fake 16-byte aligned "device" addresses
+B = 0x900000
+C = 0x1100000
+D = 0x1900000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe355.so not built")
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    names = declared_functions()
+    assert len(names) == 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(moe.exported_symbols()) == names
+
+
+def test_version_and_status_strings(L):
+    assert L.moe_abi_version() == 1
+    assert moe.moe_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert moe.moe_status_string(s) not in ("ok", "unknown status")
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+def test_route_validation(L):
+    r = L.moe_route
+    assert r(A, None, None, -1, 8, 2, B, C, None) == moe.MOE_EINVAL
+    assert r(A, None, None, 4, 8, 9, B, C, None) == moe.MOE_EINVAL          # k > E
+    assert r(A, None, None, 4, 2000, 8, B, C, None) == moe.MOE_EUNSUPPORTED  # E > 1024
+    assert r(A, None, None, 4, 64, 33, B, C, None) == moe.MOE_EUNSUPPORTED   # k > 32
+    assert r(None, None, None, 4, 8, 2, B, C, None) == moe.MOE_EINVAL
+    assert r(A, None, D, 4, 8, 2, B, C, None) == moe.MOE_EINVAL              # rows flag without bias
+    assert r(A, None, None, 4, 8, 2, B, B + 8, None) == moe.MOE_EINVAL      # outputs overlap
+    assert r(A, None, None, 0, 8, 2, B, C, None) == moe.MOE_OK               # T == 0: no-op
+    assert r(None, None, None, 0, 8, 2, None, None, None) == moe.MOE_OK
+
+
+def test_align_validation(L):
+    al = L.moe_align
+    assert al(A, 4, 8, 2, 2, B, C, D, D + 4096, None, 0, None) == moe.MOE_EINVAL       # shared not 0/1
+    assert al(A, 4, 8, 2, 1, None, C, D, D + 4096, None, 0, None) == moe.MOE_EINVAL
+    assert al(A, 4, 8, 2, 1, B, B, D, D + 4096, None, 0, None) == moe.MOE_EINVAL       # counts/offsets alias
+    T, E, k = 2000, 64, 8
+    need = L.moe_align_workspace_bytes(T, E, k)
+    assert need == 2 * E * 4
+    base = 0x10000000
+    ps = base + 0x100000
+    assert al(A, T, E, k, 1, B, C, base, ps, None, 0, None) == moe.MOE_EWORKSPACE
+    assert al(A, T, E, k, 1, B, C, base, ps, D, need - 1, None) == moe.MOE_EWORKSPACE
+    assert L.moe_align_workspace_bytes(64, 256, 8) == 0                               # single workgroup
+    assert al(A, 0, E, k, 1, B, C, base, ps, None, 0, None) == moe.MOE_OK
+
+
+def test_quant_validation(L):
+    assert L.moe_quant_rows_fp8(A, 4, 100, B, C, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_quant_rows_fp8(A + 2, 4, 128, B, C, None) == moe.MOE_EINVAL           # misaligned x
+    assert L.moe_quant_rows_fp8(A, 0, 128, B, C, None) == moe.MOE_OK
+    assert L.moe_quant_blocks_fp8(A, 2, 100, 128, B, C, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_quant_blocks_fp8(A, -1, 128, 128, B, C, None) == moe.MOE_EINVAL
+
+
+def _experts(**kw):
+    d = dict(wtype=0, E=8, H=256, I=128, has_shared=0, w1=A, w3=B, w2=C)
+    d.update(kw)
+    c = moe.moe_experts_t()
+    for k, v in d.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_gemm_validation(L):
+    g13 = L.moe_gemm13
+    x, off, sp, h = 0x20000000, 0x21000000, 0x22000000, 0x23000000
+    ok = _experts()
+    assert g13(ctypes.byref(_experts(H=100)), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EUNSUPPORTED
+    assert g13(ctypes.byref(_experts(I=200)), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EUNSUPPORTED
+    assert g13(ctypes.byref(_experts(wtype=7)), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EUNSUPPORTED
+    assert g13(ctypes.byref(_experts(wtype=1)), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(_experts(has_shared=1)), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(_experts(w2=C + 4)), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(ok), x, None, off, sp, 4, 9, h, None, None, 0, None) == moe.MOE_EINVAL       # k > E
+    assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, x, None, None, 0, None) == moe.MOE_EINVAL       # h aliases x
+    assert g13(ctypes.byref(ok), x, None, off, sp, 0, 2, h, None, None, 0, None) == moe.MOE_OK
+    assert g13(None, x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL
+    g2 = L.moe_gemm2
+    assert g2(ctypes.byref(ok), h, None, off, 4, 2, x, 3, None, 0, None) == moe.MOE_EUNSUPPORTED          # y dtype
+    assert g2(ctypes.byref(_experts(wtype=1, s1=A, s3=B, s2=C)), h, None, off, 4, 2, x, 0, None, 0, None) == moe.MOE_EINVAL
+    assert g2(ctypes.byref(ok), h, None, off, 0, 2, x, 0, None, 0, None) == moe.MOE_OK
+
+
+def test_combine_validation(L):
+    cb = L.moe_combine
+    assert cb(A, 2, B, C, 4, 2, 256, 0, D, None) == moe.MOE_EUNSUPPORTED
+    assert cb(A, 0, B, C, 4, 2, 200, 0, D, None) == moe.MOE_EUNSUPPORTED
+    assert cb(A, 0, B, C, 4, 2, 256, 3, D, None) == moe.MOE_EINVAL
+    assert cb(A, 0, B, C, 4, 2, 256, 0, A + 16, None) == moe.MOE_EINVAL    # out overlaps y
+    assert cb(A, 0, B, C, 0, 2, 256, 0, D, None) == moe.MOE_OK
+
+
+def test_forward_validation(L):
+    ex = _experts(has_shared=0)
+    need = L.moe_forward_workspace_bytes(ctypes.byref(ex), 16, 2, 0)
+    assert need > 0
+    args = moe.moe_forward_args_t(16, 2, 0, A, B, None, None, None, None, C, None, None)
+    ws = 0x40000000
+    assert L.moe_forward(ctypes.byref(ex), ctypes.byref(args), ws, need - 1, None) == moe.MOE_EWORKSPACE
+    args2 = moe.moe_forward_args_t(16, 2, 0, A, None, None, None, None, None, C, None, None)
+    assert L.moe_forward(ctypes.byref(ex), ctypes.byref(args2), ws, need, None) == moe.MOE_EINVAL   # no logits, no router
+    args3 = moe.moe_forward_args_t(16, 2, 5, A, B, None, None, None, None, C, None, None)
+    assert L.moe_forward(ctypes.byref(ex), ctypes.byref(args3), ws, need, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_forward(ctypes.byref(ex), None, ws, need, None) == moe.MOE_EINVAL
+    args0 = moe.moe_forward_args_t(0, 2, 0, None, B, None, None, None, None, None, None, None)
+    assert L.moe_forward(ctypes.byref(ex), ctypes.byref(args0), None, 0, None) == moe.MOE_OK
+
+
+def test_router_validation(L):
+    assert L.moe_router_gemm(A, B, C, D, 4, 100, 8, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_router_gemm(A, B, C, D, 4, 128, 2048, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_router_gemm(A, B, C, D, 0, 128, 8, None) == moe.MOE_OK
+    assert L.moe_router_split(A, B, B, 4, 4, None) == moe.MOE_EINVAL     # hi/lo alias
+    assert L.moe_router_split(A, B, C, 0, 4, None) == moe.MOE_OK
