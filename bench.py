@@ -1,0 +1,242 @@
+"""Benchmark of the fused MoE layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|router|tiny]
+
+A step is one pass of the whole chain (route -> align -> [quant] -> Gate-Up ->
+Down -> combine; router GEMM first for the router workload) over one batch of
+seeded synthetic input already resident in HBM.  Prints ONE JSON line.
+
+value = tokens per second of the whole layer (T tokens per step).  The
+roofline object describes the dominant kernel (the Gate-Up GEMM): its
+algorithmic bytes (or flops) per launch divided by its average launch time
+measured with HIP events on the stream it runs on.  cpu_baseline times the
+oracle on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "gemm_fp8.hip", "tiles.hpp", "common.hpp"):
+        with open(os.path.join(ROOT, "expert_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gemm13_algorithmic(wl, counts):
+    """Algorithmic bytes / flops of one Gate-Up launch.
+
+    bytes: w1 + w3 of every expert with at least one row (plus the shared
+    expert), one read of each gathered x row per slot, one write of h per slot
+    (fp8: codes + per-128 scales).  flops: 4*H*I per slot row.
+    """
+    R = wl.T * wl.k + wl.shared * wl.T
+    wb = 1 if wl.wtype == "fp8" else 2
+    touched = int((counts > 0).sum()) + wl.shared
+    weight = touched * 2 * wl.I * wl.H * wb
+    if wl.wtype == "fp8":
+        weight += touched * 2 * (wl.I // 128) * (wl.H // 128) * 4
+        act = R * (wl.H + wl.H // 128 * 4) + R * (wl.I + wl.I // 128 * 4)
+    else:
+        act = R * wl.H * 2 + R * wl.I * 2
+    flops = 4.0 * wl.H * wl.I * R
+    return weight + act, flops, touched
+
+
+def layer_flops(wl):
+    f = 6.0 * wl.H * wl.I * wl.T * (wl.k + wl.shared)
+    if wl.router:
+        f += 4.0 * wl.T * wl.H * wl.E
+    return f
+
+
+def layer_floor_bytes(wl, counts):
+    wb = 1 if wl.wtype == "fp8" else 2
+    touched = int((counts > 0).sum()) + wl.shared
+    b = touched * 3 * wl.I * wl.H * wb
+    if wl.wtype == "fp8":
+        b += touched * 3 * (wl.I // 128) * (wl.H // 128) * 4
+    b += wl.T * wl.H * 2 * 2  # x in, out
+    b += wl.T * wl.E * 4 if not wl.router else wl.E * wl.H * 4
+    return b
+
+
+def load_traffic(name, src_hash):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary,
+    only while the kernel sources are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"gemm13_{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, d, b, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    from oracle import oracle as orc
+    nthreads = orc.default_threads()
+    x = workloads.bits(d["x"])
+    logits = workloads.bits(d["logits"]) if not wl.router else workloads.bits(b.logits)
+    bias = workloads.bits(d["bias"]) if d["bias"] is not None else None
+    bias_rows = workloads.bits(d["bias_rows"]) if d["bias_rows"] is not None else None
+    if wl.wtype == "fp8":
+        return None
+    L = orc.Layer(*(workloads.bits(d[n]) if d[n] is not None else None
+                    for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")))
+    t0 = time.perf_counter()
+    ids, w = orc.route(logits, wl.k, bias, bias_rows)
+    orc.align(ids, wl.E, wl.shared)
+    t_route = time.perf_counter() - t0
+    # calibrate on 4 tokens, then size the sample to the time budget
+    rows = np.arange(min(4, wl.T), dtype=np.int64)
+    t0 = time.perf_counter()
+    orc.layer_rows(L, x, ids, w, rows, nthreads=nthreads)
+    per_tok = (time.perf_counter() - t0) / rows.size
+    n = int(max(4, min(wl.T, budget_s / max(per_tok, 1e-9))))
+    rows = np.arange(n, dtype=np.int64)
+    t0 = time.perf_counter()
+    orc.layer_rows(L, x, ids, w, rows, nthreads=nthreads)
+    t_ffn = time.perf_counter() - t0
+    per_tok = t_ffn / n
+    tok_s = 1.0 / (per_tok + t_route / wl.T)
+    return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"route+align on all {wl.T} tokens ({t_route:.3f}s); expert FFN + combine on the first "
+                      f"{n} tokens ({t_ffn:.2f}s); fp64, {nthreads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single MI355X, see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import expert_layer_amd as moe
+    from expert_layer_amd.chain import Buffers, Layer, run_chain, split_router
+
+    moe.lib()
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wl.name}: generating inputs")
+    d = workloads.make_inputs(wl, device=dev)
+    fp8 = wl.wtype == "fp8"
+    layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=fp8)
+    y_dtype = torch.float32 if wl.T * (wl.k + wl.shared) * wl.H <= (1 << 24) else torch.bfloat16
+    b = Buffers(layer, wl.T, wl.k, y_dtype=y_dtype, router=wl.router)
+    hi = lo = None
+    if wl.router:
+        hi, lo = split_router(d["router_w"])
+    kw = dict(logits=None if wl.router else d["logits"], router_hi=hi, router_lo=lo, bias=d["bias"],
+              bias_rows=d["bias_rows"])
+    if fp8:   # fp8 weights are quantised once; the bf16 copies are not needed any more
+        for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2"):
+            d[n] = None
+        torch.cuda.empty_cache()
+
+    stream = torch.cuda.current_stream()
+    names = (["router"] if wl.router else []) + ["route", "align"] + (["quant"] if fp8 else []) + \
+        ["gemm13", "gemm2", "combine"]
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run_chain(layer, b, d["x"], wl.k, **kw)
+    torch.cuda.synchronize()
+    counts = b.counts.cpu().numpy()
+
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        run_chain(layer, b, d["x"], wl.k, stages=ev[i], **kw)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in ev])) for n in names}
+    log("[bench] per-stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()) +
+        f"; step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms)")
+
+    value = wl.T / (ms_step * 1e-3)
+    g13_bytes, g13_flops, touched = gemm13_algorithmic(wl, counts)
+    g13_s = stage_ms["gemm13"] * 1e-3
+    src_hash = kernel_source_hash()
+    if wl.name in ("decode", "tiny"):
+        achieved = g13_bytes / g13_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(wl.name, src_hash)}
+    else:
+        peak = MFMA_PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+        achieved = g13_flops / g13_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": load_traffic(wl.name, src_hash)}
+    roof["kernel"] = "gemm13"
+    roof["per_launch"] = {"bytes": g13_bytes, "flops": g13_flops, "touched_experts": touched,
+                          "avg_ms": stage_ms["gemm13"]}
+    floor = layer_floor_bytes(wl, counts)
+    lf = layer_flops(wl)
+    layer_info = {"ms": ms_step, "tflops": lf / (ms_step * 1e-3) / 1e12,
+                  "hbm_floor_gbs": floor / (ms_step * 1e-3) / 1e9,
+                  "hbm_frac": floor / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "mfma_frac": lf / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["fp8" if fp8 else "bf16"],
+                  "stage_ms": stage_ms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        try:
+            cpu = cpu_baseline(wl, d, b, args.cpu_budget)
+        except MemoryError:
+            cpu = None
+
+    rec = {"metric": "MoE layer tokens/s + % of HBM (decode) / MFMA (prefill) roofline, 1 GPU",
+           "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8" if fp8 else "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
+                      "shared": wl.shared, "weights": wl.wtype, "router": wl.router,
+                      "y_dtype": "f32" if y_dtype == torch.float32 else "bf16", "seed": wl.seed},
+           "roofline": roof, "layer": layer_info, "cpu_baseline": cpu,
+           "kernel_source_hash": src_hash}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

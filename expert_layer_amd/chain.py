@@ -1,0 +1,130 @@
+"""Host-side plumbing for one MoE layer call: device buffers plus the stage
+calls in chain order.  Allocation uses torch; every computation is a call into
+libmoe355.
+
+    layer = Layer.from_weights(w1, w3, w2, sw1, sw3, sw2, fp8=False)
+    bufs = Buffers(layer, T, k, y_dtype=torch.float32)
+    run_chain(layer, bufs, x, k, logits=logits)          # or router_hi/lo=...
+    bufs.out                                             # [T, H] bf16
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (Experts, moe_align, moe_align_workspace_bytes, moe_combine, moe_gemm2, moe_gemm13,
+               moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_route, moe_router_gemm, moe_router_split)
+
+
+@dataclass
+class Layer:
+    experts: Experts
+    fp8: bool
+    E: int
+    H: int
+    I: int
+    shared: int
+
+    @staticmethod
+    def from_weights(w1, w3, w2, sw1=None, sw3=None, sw2=None, fp8=False):
+        """bf16 weights as given; fp8 quantises them once with 128x128 block scales."""
+        E, I, H = w1.shape
+        if not fp8:
+            ex = Experts(w1, w3, w2, sw1, sw3, sw2)
+            return Layer(ex, False, E, H, I, int(sw1 is not None))
+        q = {}
+        for name, w in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
+            if w is None:
+                q[name] = None
+                continue
+            rows, cols = w.shape[-2:]
+            qt = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+            st = torch.empty(w.shape[:-2] + (rows // 128, cols // 128), dtype=torch.float32, device=w.device)
+            moe_quant_blocks_fp8(w.contiguous(), qt, st)
+            q[name] = (qt, st)
+        sc = lambda n: None if q[n] is None else q[n][1]   # noqa: E731
+        co = lambda n: None if q[n] is None else q[n][0]   # noqa: E731
+        ex = Experts(co("w1"), co("w3"), co("w2"), co("sw1"), co("sw3"), co("sw2"),
+                     sc("w1"), sc("w3"), sc("w2"), sc("sw1"), sc("sw3"), sc("sw2"))
+        return Layer(ex, True, E, H, I, int(sw1 is not None))
+
+
+class Buffers:
+    """Every intermediate of one layer call for T tokens, on the weights' device."""
+
+    def __init__(self, layer: Layer, T: int, k: int, y_dtype=torch.float32, device=None, router=False):
+        dev = device or layer.experts.tensors["w1"].device
+        E, H, I = layer.E, layer.H, layer.I
+        P = T * k
+        R = P + layer.shared * T
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.T, self.k, self.R = T, k, R
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev) if router else None
+        self.ids = torch.empty((T, k), **i32)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 2, **i32)
+        self.slot_pair = torch.empty(max(P, 1), **i32)
+        self.pair_slot = torch.empty(max(P, 1), **i32)
+        nws = moe_align_workspace_bytes(T, E, k)
+        self.align_ws = torch.empty(max(nws // 4, 1), **i32)
+        if layer.fp8:
+            self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+            self.h = torch.empty((R, I), dtype=torch.uint8, device=dev)
+            self.hs = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
+        else:
+            self.xq = self.xs = self.hs = None
+            self.h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((R, H), dtype=y_dtype, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+
+def split_router(router_w):
+    """Offline split of fp32 router weights [E,H] into bf16 hi / lo parts."""
+    hi = torch.empty(router_w.shape, dtype=torch.bfloat16, device=router_w.device)
+    lo = torch.empty_like(hi)
+    moe_router_split(router_w.contiguous(), hi, lo)
+    return hi, lo
+
+
+def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, router_lo=None, bias=None,
+              bias_rows=None, stages=None):
+    """Enqueue the chain on torch's current stream.  ``stages`` (optional) maps a
+    stage name to a (start_event, end_event) pair recorded around that stage."""
+    def ev(name, i):
+        if stages is not None and name in stages:
+            stages[name][i].record()
+
+    T = x.shape[0]
+    if logits is None:
+        ev("router", 0)
+        moe_router_gemm(x, router_hi, router_lo, b.logits)
+        ev("router", 1)
+        logits = b.logits
+    ev("route", 0)
+    moe_route(logits, k, b.ids, b.w, bias=bias, bias_rows=bias_rows)
+    ev("route", 1)
+    ev("align", 0)
+    moe_align(b.ids, layer.E, layer.shared, b.counts, b.offsets, b.slot_pair, b.pair_slot, b.align_ws)
+    ev("align", 1)
+    ex = layer.experts
+    if layer.fp8:
+        ev("quant", 0)
+        moe_quant_rows_fp8(x, b.xq, b.xs)
+        ev("quant", 1)
+        ev("gemm13", 0)
+        moe_gemm13(ex, b.xq, b.xs, b.offsets, b.slot_pair, T, k, b.h, b.hs)
+        ev("gemm13", 1)
+    else:
+        ev("gemm13", 0)
+        moe_gemm13(ex, x, None, b.offsets, b.slot_pair, T, k, b.h)
+        ev("gemm13", 1)
+    ev("gemm2", 0)
+    moe_gemm2(ex, b.h, b.hs, b.offsets, T, k, b.y)
+    ev("gemm2", 1)
+    ev("combine", 0)
+    moe_combine(b.y, b.pair_slot, b.w, T, k, layer.shared, b.out)
+    ev("combine", 1)
+    return b

@@ -230,25 +230,26 @@ void orc_quant_rows_fp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, f
 // implementation item 4): for each matrix [rows, cols] and each 128x128 block,
 // scale = amax / 448 (fp32), code = e4m3(fp32(w / scale)).  s has shape
 // [mats, rows/128, cols/128].
-void orc_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s) {
-  int rb = rows / 128, cb = cols / 128;
-  for (int64_t m = 0; m < mats; ++m)
-    for (int bi = 0; bi < rb; ++bi)
-      for (int bj = 0; bj < cb; ++bj) {
-        float amax = 0.0f;
-        for (int i = 0; i < 128; ++i)
-          for (int j = 0; j < 128; ++j) {
-            int64_t idx = (m * rows + bi * 128 + i) * (int64_t)cols + bj * 128 + j;
-            amax = std::max(amax, static_cast<float>(std::fabs(bf16_value(w[idx]))));
-          }
-        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-        s[(m * rb + bi) * cb + bj] = sc;
-        for (int i = 0; i < 128; ++i)
-          for (int j = 0; j < 128; ++j) {
-            int64_t idx = (m * rows + bi * 128 + i) * (int64_t)cols + bj * 128 + j;
-            q[idx] = e4m3_code(static_cast<float>(bf16_value(w[idx])) / sc);
-          }
+void orc_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s,
+                          int nthreads) {
+  const int rb = rows / 128, cb = cols / 128;
+  parallel_for(mats * rb * cb, nthreads, [&](int64_t b) {
+    const int64_t m = b / ((int64_t)rb * cb);
+    const int bi = (int)((b / cb) % rb), bj = (int)(b % cb);
+    float amax = 0.0f;
+    for (int i = 0; i < 128; ++i)
+      for (int j = 0; j < 128; ++j) {
+        int64_t idx = (m * rows + bi * 128 + i) * (int64_t)cols + bj * 128 + j;
+        amax = std::max(amax, static_cast<float>(std::fabs(bf16_value(w[idx]))));
       }
+    float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    s[b] = sc;
+    for (int i = 0; i < 128; ++i)
+      for (int j = 0; j < 128; ++j) {
+        int64_t idx = (m * rows + bi * 128 + i) * (int64_t)cols + bj * 128 + j;
+        q[idx] = e4m3_code(static_cast<float>(bf16_value(w[idx])) / sc);
+      }
+  });
 }
 
 // ---------------------------------------------------------------- expert FFN

@@ -65,7 +65,7 @@ def lib():
         L.orc_route.argtypes = [_P, _P, _P, _I64, _I32, _I32, _P, _P]
         L.orc_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
         L.orc_quant_rows_fp8.argtypes = [_P, _I64, _I32, _P, _P]
-        L.orc_quant_blocks_fp8.argtypes = [_P, _I64, _I32, _I32, _P, _P]
+        L.orc_quant_blocks_fp8.argtypes = [_P, _I64, _I32, _I32, _P, _P, _I32]
         L.orc_expert_bf16.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_expert_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_layer_rows.argtypes = [ctypes.POINTER(_Layer), _P, _P, _P, _P, _I32, _P, _I64, _P, _I32]
@@ -156,7 +156,7 @@ def quant_rows_fp8(x_bits):
     return q, s
 
 
-def quant_blocks_fp8(w_bits):
+def quant_blocks_fp8(w_bits, nthreads=None):
     """w_bits: [mats, rows, cols] (or [rows, cols]) bf16 bit patterns."""
     w_bits = _c(w_bits, np.uint16)
     squeeze = w_bits.ndim == 2
@@ -165,7 +165,7 @@ def quant_blocks_fp8(w_bits):
     mats, rows, cols = w_bits.shape
     q = np.empty(w_bits.shape, np.uint8)
     s = np.empty((mats, rows // 128, cols // 128), np.float32)
-    lib().orc_quant_blocks_fp8(_ptr(w_bits), mats, rows, cols, _ptr(q), _ptr(s))
+    lib().orc_quant_blocks_fp8(_ptr(w_bits), mats, rows, cols, _ptr(q), _ptr(s), nthreads or default_threads())
     return (q[0], s[0]) if squeeze else (q, s)
 
 

@@ -1,0 +1,148 @@
+"""Shared GPU-vs-oracle checking for the parity tests.
+
+The HIP chain runs through the C ABI (via the ctypes binding); the oracle runs
+on the host copies of the identical input bytes.  Tolerances:
+  * route ids, align outputs, fp8 codes/scales: bit-exact;
+  * routing weights: |dw| <= 1e-6 (fp32 exp on the GPU vs fp64);
+  * layer output: max|out - ref| <= 1e-2 max|ref| (bf16), 5e-2 max|ref| (fp8,
+    against the oracle that emulates the quantisation steps exactly);
+  * router logits: max|dl| <= 1e-5 max|ref| over [T,E] against fp64.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads
+from expert_layer_amd.chain import Buffers, Layer, run_chain, split_router
+from oracle import oracle as orc
+
+TOL = {"bf16": 1e-2, "fp8": 5e-2}
+
+
+def log(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return None if t is None else workloads.bits(t)
+
+
+def run_gpu(wl, d, y_dtype=torch.float32):
+    fp8 = wl.wtype == "fp8"
+    layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=fp8)
+    b = Buffers(layer, wl.T, wl.k, y_dtype=y_dtype, router=wl.router)
+    hi = lo = None
+    if wl.router:
+        hi, lo = split_router(d["router_w"])
+    run_chain(layer, b, d["x"], wl.k, logits=None if wl.router else d["logits"], router_hi=hi, router_lo=lo,
+              bias=d["bias"], bias_rows=d["bias_rows"])
+    torch.cuda.synchronize()
+    return layer, b, (hi, lo)
+
+
+def checked_rows(wl, counts, offsets, slot_pair, nsample=256):
+    """All rows for small T; else a seeded sample plus the first token of every touched expert."""
+    if wl.T <= 512:
+        return np.arange(wl.T, dtype=np.int64)
+    rows = set(workloads.sample_rows(wl.T, nsample, wl.seed + 7).tolist())
+    for e in range(wl.E):
+        if counts[e] > 0:
+            rows.add(int(slot_pair[offsets[e]]) // wl.k)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def check_layer(wl, d, y_dtype=torch.float32, check_rows=None):
+    """Run the chain on the GPU and compare every stage with the oracle."""
+    t0 = time.time()
+    log(f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I} S={wl.shared} {wl.wtype} y={y_dtype}")
+    layer, b, (hi, lo) = run_gpu(wl, d, y_dtype)
+    k, E = wl.k, wl.E
+    x = host(d["x"])
+    bias = host(d["bias"])
+    bias_rows = host(d["bias_rows"])
+
+    # ---- router front end
+    if wl.router:
+        w = host(d["router_w"])
+        rhi, rlo = orc.router_split(w)
+        assert np.array_equal(host(hi), rhi), "router split hi"
+        assert np.array_equal(host(lo), rlo), "router split lo"
+        glog = host(b.logits)
+        ref = orc.router_logits(x, w)
+        err = np.abs(glog.astype(np.float64) - ref).max()
+        assert err <= 1e-5 * np.abs(ref).max(), f"router logits err {err} vs {np.abs(ref).max()}"
+        logits = glog            # routing is evaluated on the GPU's logits
+        ref_ids_exact, _ = orc.route(ref.astype(np.float32), k, bias, bias_rows)
+    else:
+        logits = host(d["logits"])
+
+    # ---- route
+    ids_ref, w_ref = orc.route(logits, k, bias, bias_rows)
+    ids = host(b.ids)
+    wts = host(b.w)
+    assert np.array_equal(ids, ids_ref), f"route ids differ in {np.sum(ids != ids_ref)} entries"
+    werr = np.abs(wts.astype(np.float64) - w_ref).max()
+    assert werr <= 1e-6, f"route weights err {werr}"
+    if wl.router:
+        frac = np.mean(np.any(np.sort(ref_ids_exact, 1) != np.sort(ids_ref, 1), axis=1))
+        log(f"  tokens whose top-k set differs under exact logits: {frac:.5f}")
+
+    # ---- align
+    counts, offsets, sp, ps = orc.align(ids_ref, E, wl.shared)
+    assert np.array_equal(host(b.counts), counts), "align counts"
+    assert np.array_equal(host(b.offsets), offsets), "align offsets"
+    P = wl.T * k
+    assert np.array_equal(host(b.slot_pair)[:P], sp), "align slot_pair"
+    assert np.array_equal(host(b.pair_slot)[:P], ps), "align pair_slot"
+
+    rows = checked_rows(wl, counts, offsets, sp) if check_rows is None else check_rows
+
+    # ---- experts (oracle on the checked rows)
+    if wl.wtype == "fp8":
+        xq_ref, xs_ref = orc.quant_rows_fp8(x)
+        assert np.array_equal(host(b.xq), xq_ref), "x quant codes"
+        assert np.array_equal(host(b.xs), xs_ref), "x quant scales"
+        used = np.unique(ids_ref[rows].ravel())
+        ex = layer.experts.tensors
+        qs = {}
+        for name in ("w1", "w3", "w2"):
+            src = d[name][torch.from_numpy(used).to(d[name].device)]
+            q, s = orc.quant_blocks_fp8(host(src))
+            assert np.array_equal(host(ex[name][torch.from_numpy(used).to(d[name].device)]), q), f"{name} codes"
+            sname = "s" + name[1:]
+            assert np.array_equal(host(ex[sname][torch.from_numpy(used).to(d[name].device)]), s), f"{name} scales"
+            qs[name] = (q, s)
+        sq = {}
+        if wl.shared:
+            for name in ("sw1", "sw3", "sw2"):
+                q, s = orc.quant_blocks_fp8(host(d[name]))
+                assert np.array_equal(host(ex[name]), q), f"{name} codes"
+                assert np.array_equal(host(ex["ss" + name[2:]]), s), f"{name} scales"
+                sq[name] = (q, s)
+        remap = np.full(E, -1, np.int32)
+        remap[used] = np.arange(used.size, dtype=np.int32)
+        L = orc.Layer(qs["w1"][0], qs["w3"][0], qs["w2"][0],
+                      sq["sw1"][0] if wl.shared else None, sq["sw3"][0] if wl.shared else None,
+                      sq["sw2"][0] if wl.shared else None, wtype=1,
+                      s1=qs["w1"][1], s3=qs["w3"][1], s2=qs["w2"][1],
+                      ss1=sq["sw1"][1] if wl.shared else None, ss3=sq["sw3"][1] if wl.shared else None,
+                      ss2=sq["sw2"][1] if wl.shared else None)
+        ids_c = ids_ref.copy()
+        ids_c[rows] = remap[ids_ref[rows]]
+        ref = orc.layer_rows(L, xq_ref, ids_c, w_ref, rows, xs=xs_ref)
+    else:
+        L = orc.Layer(host(d["w1"]), host(d["w3"]), host(d["w2"]), host(d["sw1"]), host(d["sw3"]), host(d["sw2"]))
+        ref = orc.layer_rows(L, x, ids_ref, w_ref, rows)
+    out = b.out.float().cpu().numpy()[rows]
+    err = np.abs(out - ref).max()
+    scale = np.abs(ref).max()
+    tol = TOL[wl.wtype]
+    log(f"  rows checked {rows.size}, max|err| {err:.3e}, max|ref| {scale:.3e}, ratio {err / scale:.3e} "
+        f"(tol {tol}), {time.time() - t0:.1f}s")
+    assert err <= tol * scale, f"layer output err {err} > {tol} * {scale}"
+    return layer, b
