@@ -20,7 +20,6 @@ namespace moe355 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kD = 4;  // k-steps of 32 in flight per wave
 
 __device__ __forceinline__ bf16x8_t ld8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
@@ -31,7 +30,13 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 }
 
 // ---------------------------------------------------------------- Gate-Up
-template <int MT>
+// K loop shape shared by both kernels: stages 0..D-1 are loaded up front; the
+// steady-state loop consumes stage s and immediately refills it D steps ahead
+// with no data-dependent control flow (so the compiler can keep D k-steps of
+// loads in flight and wait with vmcnt(N > 0)); the last D steps drain.
+// Rows past the end of a chunk read a valid clamped row; their results are
+// never stored.
+template <int MT, int D>
 __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint16_t* __restrict__ x,
                                                           uint16_t* __restrict__ h) {
   __shared__ ChunkTable tab;
@@ -43,7 +48,6 @@ __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint
   const int64_t P = a.T * a.k;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-  const bf16x8_t zero = {};
 
   for (int64_t it = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); it < items; it += nwaves) {
     const int c = (int)(it / NT);
@@ -51,7 +55,6 @@ __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint
     const int g = chunk_group(tab, G, c);
     const int r0 = a.offsets[g] + (c - tab.prefix[g]) * 16 * MT;
     const int rend = min(r0 + 16 * MT, a.offsets[g + 1]);
-    const int nmt = (rend - r0 + 15) / 16;
     const bool shared = g == a.E;
     const uint16_t* w1 = shared ? static_cast<const uint16_t*>(a.sw1)
                                 : static_cast<const uint16_t*>(a.w1) + (int64_t)g * I * H;
@@ -62,12 +65,9 @@ __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint
     const uint16_t* ap[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int r = r0 + mt * 16 + lr;
-      ap[mt] = nullptr;
-      if (mt < nmt && r < rend) {
-        const int64_t t = r < P ? (int64_t)(a.slot_pair[r] / a.k) : (int64_t)r - P;
-        ap[mt] = x + t * H + lq * 8;
-      }
+      const int r = min(r0 + mt * 16 + lr, rend - 1);
+      const int64_t t = r < P ? (int64_t)(a.slot_pair[r] / a.k) : (int64_t)r - P;
+      ap[mt] = x + t * H + lq * 8;
     }
     f32x4_t accg[MT], accu[MT];
 #pragma unroll
@@ -75,31 +75,36 @@ __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint
       accg[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    bf16x8_t bg[kD], bu[kD], av[kD][MT];
+    bf16x8_t bg[D], bu[D], av[D][MT];
 #pragma unroll
-    for (int s = 0; s < kD; ++s) {
+    for (int s = 0; s < D; ++s) {
       bg[s] = ld8(b1 + 32 * s);
       bu[s] = ld8(b3 + 32 * s);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[s][mt] = ap[mt] ? ld8(ap[mt] + 32 * s) : zero;
+      for (int mt = 0; mt < MT; ++mt) av[s][mt] = ld8(ap[mt] + 32 * s);
     }
-    for (int k0 = 0; k0 < H; k0 += 32 * kD) {
+    int k0 = 0;
+    for (; k0 < H - 32 * D; k0 += 32 * D) {
 #pragma unroll
-      for (int s = 0; s < kD; ++s) {
+      for (int s = 0; s < D; ++s) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          if (mt < nmt) {
-            accg[mt] = mfma16(av[s][mt], bg[s], accg[mt]);
-            accu[mt] = mfma16(av[s][mt], bu[s], accu[mt]);
-          }
+          accg[mt] = mfma16(av[s][mt], bg[s], accg[mt]);
+          accu[mt] = mfma16(av[s][mt], bu[s], accu[mt]);
         }
-        const int kn = k0 + 32 * (s + kD);
-        if (kn < H) {
-          bg[s] = ld8(b1 + kn);
-          bu[s] = ld8(b3 + kn);
+        const int kn = k0 + 32 * (s + D);
+        bg[s] = ld8(b1 + kn);
+        bu[s] = ld8(b3 + kn);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[s][mt] = ap[mt] ? ld8(ap[mt] + kn) : zero;
-        }
+        for (int mt = 0; mt < MT; ++mt) av[s][mt] = ld8(ap[mt] + kn);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        accg[mt] = mfma16(av[s][mt], bg[s], accg[mt]);
+        accu[mt] = mfma16(av[s][mt], bu[s], accu[mt]);
       }
     }
 #pragma unroll
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + mt * 16 + lq * 4 + i;
-        if (mt < nmt && r < rend)
+        if (r < rend)
           h[(int64_t)r * I + n0 + lr] = (uint16_t)f32_to_bf16(silu_mul(accg[mt][i], accu[mt][i]));
       }
     }
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void gemm13_stream(GemmArgs a, const uint
 }
 
 // ---------------------------------------------------------------- Down
-template <int MT, int YBF16>
+template <int MT, int D, int YBF16>
 __global__ __launch_bounds__(kThreads) void gemm2_stream(GemmArgs a, const uint16_t* __restrict__ h,
                                                          void* __restrict__ y) {
   __shared__ ChunkTable tab;
@@ -126,7 +131,6 @@ __global__ __launch_bounds__(kThreads) void gemm2_stream(GemmArgs a, const uint1
   const int64_t items = (int64_t)nchunks * NT;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-  const bf16x8_t zero = {};
 
   for (int64_t it = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); it < items; it += nwaves) {
     const int c = (int)(it / NT);
@@ -134,46 +138,48 @@ __global__ __launch_bounds__(kThreads) void gemm2_stream(GemmArgs a, const uint1
     const int g = chunk_group(tab, G, c);
     const int r0 = a.offsets[g] + (c - tab.prefix[g]) * 16 * MT;
     const int rend = min(r0 + 16 * MT, a.offsets[g + 1]);
-    const int nmt = (rend - r0 + 15) / 16;
     const uint16_t* w2 = g == a.E ? static_cast<const uint16_t*>(a.sw2)
                                   : static_cast<const uint16_t*>(a.w2) + (int64_t)g * H * I;
     const uint16_t* b2 = w2 + (int64_t)(n0 + lr) * I + lq * 8;
     const uint16_t* ap[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int r = r0 + mt * 16 + lr;
-      ap[mt] = (mt < nmt && r < rend) ? h + (int64_t)r * I + lq * 8 : nullptr;
+      const int r = min(r0 + mt * 16 + lr, rend - 1);
+      ap[mt] = h + (int64_t)r * I + lq * 8;
     }
     f32x4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t bw[kD], av[kD][MT];
+    bf16x8_t bw[D], av[D][MT];
 #pragma unroll
-    for (int s = 0; s < kD; ++s) {
+    for (int s = 0; s < D; ++s) {
       bw[s] = ld8(b2 + 32 * s);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[s][mt] = ap[mt] ? ld8(ap[mt] + 32 * s) : zero;
+      for (int mt = 0; mt < MT; ++mt) av[s][mt] = ld8(ap[mt] + 32 * s);
     }
-    for (int k0 = 0; k0 < I; k0 += 32 * kD) {
+    int k0 = 0;
+    for (; k0 < I - 32 * D; k0 += 32 * D) {
 #pragma unroll
-      for (int s = 0; s < kD; ++s) {
+      for (int s = 0; s < D; ++s) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          if (mt < nmt) acc[mt] = mfma16(av[s][mt], bw[s], acc[mt]);
-        const int kn = k0 + 32 * (s + kD);
-        if (kn < I) {
-          bw[s] = ld8(b2 + kn);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(av[s][mt], bw[s], acc[mt]);
+        const int kn = k0 + 32 * (s + D);
+        bw[s] = ld8(b2 + kn);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) av[s][mt] = ap[mt] ? ld8(ap[mt] + kn) : zero;
-        }
+        for (int mt = 0; mt < MT; ++mt) av[s][mt] = ld8(ap[mt] + kn);
       }
+    }
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(av[s][mt], bw[s], acc[mt]);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + mt * 16 + lq * 4 + i;
-        if (mt < nmt && r < rend) {
+        if (r < rend) {
           if (YBF16)
             static_cast<uint16_t*>(y)[(int64_t)r * H + n0 + lr] = (uint16_t)f32_to_bf16(acc[mt][i]);
           else
@@ -191,27 +197,35 @@ bool small_groups(const GemmArgs& a) { return a.T * a.k <= (int64_t)a.E * 16; }
 
 }  // namespace
 
+// The K loops need K % (32 * D) == 0: D = 8 when K is a multiple of 256,
+// otherwise D = 4 (K is always a multiple of 128).
 hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
-  if (small_groups(a))
-    gemm13_stream<1><<<stream_grid(), kThreads, 0, s>>>(a, x, h);
+  const bool deep = a.H % 256 == 0;
+  if (!small_groups(a))
+    gemm13_stream<4, 4><<<stream_grid(), kThreads, 0, s>>>(a, x, h);
+  else if (deep)
+    gemm13_stream<1, 8><<<stream_grid(), kThreads, 0, s>>>(a, x, h);
   else
-    gemm13_stream<4><<<stream_grid(), kThreads, 0, s>>>(a, x, h);
+    gemm13_stream<1, 4><<<stream_grid(), kThreads, 0, s>>>(a, x, h);
   return hipGetLastError();
 }
 
+template <int YBF16>
+void gemm2_dispatch(const GemmArgs& a, const uint16_t* h, void* y, hipStream_t s) {
+  const bool deep = a.I % 256 == 0;
+  if (!small_groups(a))
+    gemm2_stream<4, 4, YBF16><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
+  else if (deep)
+    gemm2_stream<1, 8, YBF16><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
+  else
+    gemm2_stream<1, 4, YBF16><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
+}
+
 hipError_t launch_gemm2_bf16(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s) {
-  const bool sm = small_groups(a);
-  if (y_dtype == 1) {
-    if (sm)
-      gemm2_stream<1, 1><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
-    else
-      gemm2_stream<4, 1><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
-  } else {
-    if (sm)
-      gemm2_stream<1, 0><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
-    else
-      gemm2_stream<4, 0><<<stream_grid(), kThreads, 0, s>>>(a, h, y);
-  }
+  if (y_dtype == 1)
+    gemm2_dispatch<1>(a, h, y, s);
+  else
+    gemm2_dispatch<0>(a, h, y, s);
   return hipGetLastError();
 }
 
