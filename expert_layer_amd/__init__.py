@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe355.so")
+# MOE355_LIB may point at another build of the same library (e.g. a tuned variant)
+LIB_PATH = os.environ.get("MOE355_LIB") or os.path.join(_PKG, "libmoe355.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EDEVICE = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1

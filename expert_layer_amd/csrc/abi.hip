@@ -4,7 +4,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/moe355.h"
+#include "moe355.h"
 #include "common.hpp"
 
 namespace moe355 {

@@ -260,12 +260,15 @@ int stream_grid() { return device_cus() * 8; }
 
 // Rows per chunk: 16 when groups are small (decode-shaped), 64 otherwise.
 bool small_groups(const GemmArgs& a) { return a.T * a.k <= (int64_t)a.E * 16; }
+// Groups of 64+ rows on average go to the LDS-tiled MFMA kernels.
+bool large_groups(const GemmArgs& a) { return a.T * a.k >= (int64_t)a.E * 64; }
 
 }  // namespace
 
 // The K loops need K % (64 * D) == 0: D = 4 when K is a multiple of 256,
 // otherwise D = 2 (K is always a multiple of 128).
 hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
+  if (large_groups(a) && tiled_gemm13_ok(a)) return launch_gemm13_tiled(a, x, h, s);
   const bool deep = a.H % 256 == 0;
   if (!small_groups(a))
     gemm13_stream<4, 2><<<stream_grid(), kThreads, 0, s>>>(a, x, h);
@@ -288,6 +291,7 @@ void gemm2_dispatch(const GemmArgs& a, const uint16_t* h, void* y, hipStream_t s
 }
 
 hipError_t launch_gemm2_bf16(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s) {
+  if (large_groups(a) && tiled_gemm2_ok(a)) return launch_gemm2_tiled(a, h, y, y_dtype, s);
   if (y_dtype == 1)
     gemm2_dispatch<1>(a, h, y, s);
   else

@@ -1,0 +1,293 @@
+// Grouped expert GEMMs for large groups (prefill-shaped batches): LDS-tiled
+// bf16 MFMA kernels, fp32 accumulation.
+//
+// FusedMoE stages 2-3 (Gate-Up with SwiGLU) and 4 (Down) of the HPC-Ops page
+// (main functions / technical principles): the Gate-Up A rows are gathered
+// straight from x through the routing index (no gathered copy), the same
+// waves load and compute (no warp specialisation) and latency is hidden by a
+// multi-stage LDS ring instead.
+//
+// Tile: up to 256 rows of one group x 256 weight rows (Gate-Up: 128 gate +
+// 128 up columns of h; Down: 256 columns of y), 32 k per stage, a ring of 4
+// stages in LDS (128 KB, one workgroup per CU).  Stages are filled with the
+// gfx950 direct-to-LDS 16-byte loads: each load instruction writes 1 KB of
+// LDS (16 rows x 64 B) and every lane picks the global address whose 16 bytes
+// belong at its LDS slot, which realises the XOR swizzle that keeps MFMA
+// fragment reads free of bank conflicts.
+//
+// Eight waves, two per SIMD, in a 2 (rows) x 4 (weight rows) grid: wave w
+// computes rows 128*(w/4) .. +127 against 64 weight rows (Gate-Up: gate
+// columns 32*(w%4) .. +31 and the matching up columns).  Waves are dealt to
+// SIMDs round robin, so waves w and w+4 share a SIMD and a weight slice: a
+// tile of up to 128 rows still keeps every SIMD's matrix core busy, and
+// 16-row fragments past the tile's valid rows are skipped.  A group with r
+// rows is cut into full 256-row tiles and a remainder tile.
+//
+// Items (m-tile, n-tile) are ordered group by group, n-tile by n-tile, with
+// the m-tiles of one (group, n-tile) adjacent; a persistent grid of one
+// workgroup per CU strides over them, and the physical workgroup -> worker
+// mapping keeps consecutive workers on the same XCD (workgroups are dealt to
+// the 8 XCDs round robin), so m-tiles that share a weight tile share that
+// XCD's L2.
+#include "tiles.hpp"
+
+namespace moe355 {
+
+namespace {
+
+constexpr int kTM = 256;      // max rows per tile
+constexpr int kTN = 256;      // weight rows per tile
+constexpr int kTK = 32;       // k per stage
+constexpr int kStages = 4;    // LDS ring depth
+constexpr int kThreads = 512;  // 8 waves, two per SIMD
+constexpr int kRowSlots = kTK * 2 / 16;  // 16-byte slots per row per stage (4)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte slot of (row, chunk) inside a 64-byte row.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct TileTable {
+  int prefix[kMaxGroups + 1];  // m-tiles in groups < g
+  int wsum[16];
+};
+
+// Tile t of a group of `cnt` rows: full 256-row tiles, then the remainder
+// (fragments past the valid rows are skipped, so a short remainder costs
+// little matrix-core time; its weight tile is read again, from the L2 of the
+// XCD that runs the group's full tiles next to it).
+__device__ __forceinline__ void tile_rows(int cnt, int t, int& start, int& rows) {
+  start = t * kTM;
+  rows = min(kTM, cnt - start);
+}
+
+template <int MODE, int YBF16>  // MODE 0: Gate-Up (+SwiGLU, h bf16); MODE 1: Down (y)
+__global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint16_t* __restrict__ A,
+                                                          void* __restrict__ out) {
+  // one named array per ring stage: the stage being read and the stages being
+  // filled are then provably distinct objects, so reads wait only for their own stage
+  __shared__ __attribute__((aligned(1024))) i32x4_t a0[kTM * kRowSlots], a1[kTM * kRowSlots],
+      a2[kTM * kRowSlots], a3[kTM * kRowSlots];
+  __shared__ __attribute__((aligned(1024))) i32x4_t b0[kTN * kRowSlots], b1[kTN * kRowSlots],
+      b2[kTN * kRowSlots], b3[kTN * kRowSlots];
+  __shared__ ChunkTable tab;
+
+  const int G = a.E + (a.has_shared ? 1 : 0);
+  const int nmt_total = build_chunks(tab, a.offsets, G, kTM);
+  const int H = a.H, I = a.I;
+  const int K = MODE == 0 ? H : I;            // reduction length
+  const int NT = MODE == 0 ? (2 * I) / kTN : H / kTN;
+  const int64_t items = (int64_t)nmt_total * NT;
+  const int64_t P = a.T * a.k;
+  const int nk = K / kTK;
+
+  // the wave index feeds the LDS destination of the direct loads (M0), so make it provably uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  // direct-to-LDS role: load i (0, 1) of this wave fills rows 16*(2*wave+i) + lane/4,
+  // slot lane%4 (which holds chunk slot ^ swz(row))
+  const int lrow = lane >> 2, lslot = lane & 3;
+
+  // XCD-aware worker id: workgroup b runs on XCD b % 8
+  const int nblk = gridDim.x;
+  const int per_xcd = nblk / 8;
+  const int b = blockIdx.x;
+  const int worker = (nblk % 8 == 0) ? (b % 8) * per_xcd + b / 8 : b;
+
+  for (int64_t it = worker; it < items; it += nblk) {
+    // ---- item -> (group, n-tile, m-tile); items of group g start at prefix[g] * NT
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)tab.prefix[mid] * NT <= it) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int mtg = tab.prefix[g + 1] - tab.prefix[g];
+    const int local = (int)(it - (int64_t)tab.prefix[g] * NT);
+    const int nt = local / mtg, mt = local % mtg;
+    const int cnt = a.offsets[g + 1] - a.offsets[g];
+    int rs, nrows;
+    tile_rows(cnt, mt, rs, nrows);
+    const int r0 = a.offsets[g] + rs;
+    const int nmf = (nrows + 15) >> 4;   // valid 16-row fragments
+    const bool shared = g == a.E;
+
+    // ---- per-lane global addresses for the direct-to-LDS loads (element offsets)
+    int a_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 16 * (2 * wave + i) + lrow;
+      const int r = r0 + min(row, nrows - 1);
+      int64_t base;
+      if (MODE == 0) {
+        const int64_t t = r < P ? (int64_t)(a.slot_pair[r] / a.k) : (int64_t)r - P;
+        base = t * H;
+      } else {
+        base = (int64_t)r * I;
+      }
+      a_off[i] = (int)base + ((lslot ^ swz(row)) * 8);
+    }
+    const uint16_t* bw;   // weight rows of this wave's loads
+    int b_off[2];
+    if (MODE == 0) {
+      const int half = wave >> 2;  // waves 0-3 load gate rows, waves 4-7 up rows
+      const uint16_t* wm = half == 0 ? static_cast<const uint16_t*>(shared ? a.sw1 : a.w1)
+                                     : static_cast<const uint16_t*>(shared ? a.sw3 : a.w3);
+      bw = wm + (shared ? 0 : (int64_t)g * I * H) + (int64_t)(nt * (kTN / 2)) * H;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 16 * (2 * wave + i) + lrow;     // 0..255 in the B tile
+        const int wrow = row - half * (kTN / 2);        // 0..127 inside gate or up
+        b_off[i] = wrow * H + ((lslot ^ swz(row)) * 8);
+      }
+    } else {
+      const uint16_t* wm = static_cast<const uint16_t*>(shared ? a.sw2 : a.w2);
+      bw = wm + (shared ? 0 : (int64_t)g * H * I) + (int64_t)(nt * kTN) * I;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 16 * (2 * wave + i) + lrow;
+        b_off[i] = row * I + ((lslot ^ swz(row)) * 8);
+      }
+    }
+
+    auto issue = [&](int kk, i32x4_t* la, i32x4_t* lb) {
+      const int k0 = kk * kTK;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        load_lds16(A + a_off[i] + k0, &la[(2 * wave + i) * 64]);
+        load_lds16(bw + b_off[i] + k0, &lb[(2 * wave + i) * 64]);
+      }
+    };
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // B fragment rows of this wave inside the tile
+    int brow[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      brow[f] = MODE == 0 ? (f < 2 ? 32 * wn + 16 * f : kTN / 2 + 32 * wn + 16 * (f - 2)) : 64 * wn + 16 * f;
+    const int mfw = min(8, max(0, nmf - 8 * wm));  // valid fragments of this wave
+
+    // fragments past the valid rows are skipped in halves of 4 (64 rows)
+    auto compute = [&](const i32x4_t* la, const i32x4_t* lb) {
+      bf16x8_t bfr[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int row = brow[f] + lr;
+        bfr[f] = __builtin_bit_cast(bf16x8_t, lb[row * kRowSlots + (lq ^ swz(row))]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if (mfw > 4 * hf) {
+          bf16x8_t af[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int row = 128 * wm + 16 * (4 * hf + m) + lr;
+            af[m] = __builtin_bit_cast(bf16x8_t, la[row * kRowSlots + (lq ^ swz(row))]);
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[4 * hf + m][f] = mfma16(af[m], bfr[f], acc[4 * hf + m][f]);
+        }
+      }
+    };
+
+    // one stage: wait for this stage's loads (at most `ahead` later stages stay in
+    // flight, 4 loads each), barrier, refill the stage computed last time, compute
+    auto stage = [&](int kk, const i32x4_t* la, const i32x4_t* lb, i32x4_t* fa, i32x4_t* fb) {
+      const int ahead = nk - 1 - kk;
+      if (ahead >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (ahead == 1)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // execution barrier only: a fence here would also wait for the stages still
+      // in flight; the vmcnt wait above already put this stage's bytes in LDS
+      __builtin_amdgcn_s_barrier();
+      if (kk + kStages - 1 < nk) issue(kk + kStages - 1, fa, fb);
+      compute(la, lb);
+    };
+
+    // previous item's stores retired (stores also count in vmcnt) and every wave
+    // finished reading the ring before it is refilled
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(0, a0, b0);
+    if (nk > 1) issue(1, a1, b1);
+    if (nk > 2) issue(2, a2, b2);
+    // nk is a multiple of 4 (K % 128 == 0)
+    for (int kk = 0; kk < nk; kk += kStages) {
+      stage(kk + 0, a0, b0, a3, b3);
+      stage(kk + 1, a1, b1, a0, b0);
+      stage(kk + 2, a2, b2, a1, b1);
+      stage(kk + 3, a3, b3, a2, b2);
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < mfw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 128 * wm + 16 * m + 4 * lq + i;
+          if (row < nrows) {
+            const int64_t r = r0 + row;
+            if (MODE == 0) {
+              uint16_t* h = static_cast<uint16_t*>(out);
+              const int col = nt * (kTN / 2) + 32 * wn + lr;
+              h[r * I + col] = (uint16_t)f32_to_bf16(silu_mul(acc[m][0][i], acc[m][2][i]));
+              h[r * I + col + 16] = (uint16_t)f32_to_bf16(silu_mul(acc[m][1][i], acc[m][3][i]));
+            } else {
+              const int col = nt * kTN + 64 * wn + lr;
+#pragma unroll
+              for (int f = 0; f < 4; ++f) {
+                if (YBF16)
+                  static_cast<uint16_t*>(out)[r * H + col + 16 * f] = (uint16_t)f32_to_bf16(acc[m][f][i]);
+                else
+                  static_cast<float*>(out)[r * H + col + 16 * f] = acc[m][f][i];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Tiled kernels need the weight-row tile to divide the output width:
+// Gate-Up 2*I % 256 == 0 (I % 128 == 0 always holds), Down H % 256 == 0.
+bool tiled_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0; }
+bool tiled_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
+
+hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
+  gemm_tiled<0, 0><<<device_cus(), kThreads, 0, s>>>(a, x, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_tiled(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s) {
+  if (y_dtype == 1)
+    gemm_tiled<1, 1><<<device_cus(), kThreads, 0, s>>>(a, h, y);
+  else
+    gemm_tiled<1, 0><<<device_cus(), kThreads, 0, s>>>(a, h, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe355
