@@ -86,6 +86,13 @@ bool tiled_gemm2_ok(const GemmArgs& a);
 hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s);
 
+bool tiled_fp8_gemm13_ok(const GemmArgs& a);
+bool tiled_fp8_gemm2_ok(const GemmArgs& a);
+hipError_t launch_gemm13_fp8_tiled(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq, float* hs,
+                                   hipStream_t s);
+hipError_t launch_gemm2_fp8_tiled(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
+                                  hipStream_t s);
+
 hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
                           int k, int H, int has_shared, uint16_t* out, hipStream_t s);
 

@@ -258,10 +258,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_stream(GemmArgs a, const uint1
 
 int stream_grid() { return device_cus() * 8; }
 
-// Rows per chunk: 16 when groups are small (decode-shaped), 64 otherwise.
-bool small_groups(const GemmArgs& a) { return a.T * a.k <= (int64_t)a.E * 16; }
-// Groups of 64+ rows on average go to the LDS-tiled MFMA kernels.
-bool large_groups(const GemmArgs& a) { return a.T * a.k >= (int64_t)a.E * 64; }
+
 
 }  // namespace
 

@@ -230,12 +230,14 @@ __global__ __launch_bounds__(256) void gemm2_fp8_stream(GemmArgs a, const uint8_
 
 hipError_t launch_gemm13_fp8(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq, float* hs,
                              hipStream_t s) {
+  if (large_groups(a) && tiled_fp8_gemm13_ok(a)) return launch_gemm13_fp8_tiled(a, xq, xs, hq, hs, s);
   gemm13_fp8_stream<<<device_cus() * 4, 512, 0, s>>>(a, xq, xs, hq, hs);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_fp8(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
                             hipStream_t s) {
+  if (large_groups(a) && tiled_fp8_gemm2_ok(a)) return launch_gemm2_fp8_tiled(a, hq, hs, y, y_dtype, s);
   if (y_dtype == 1)
     gemm2_fp8_stream<1><<<device_cus() * 8, 256, 0, s>>>(a, hq, hs, y);
   else

@@ -49,8 +49,14 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-// XOR swizzle of the 16-byte slot of (row, chunk) inside a 64-byte row.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// XOR swizzle of the 16-byte slot of (row, chunk) inside a 64-byte row:
+// bits (b2^b3, b1^b3) of the row.  For one chunk, rows 0..7 of either parity
+// hit distinct 16-byte bank groups of a 128-byte sweep, and rows 0..15 sharing
+// their low two bits hit distinct groups of a 256-byte sweep.  Only bits 1-3
+// are used, so every 16-row fragment shares the per-lane slot offsets.
+__device__ __forceinline__ int swz(int row) {
+  return ((((row >> 2) ^ (row >> 3)) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1);
+}
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -175,30 +181,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
 #pragma unroll
       for (int f = 0; f < 4; ++f) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // B fragment rows of this wave inside the tile
-    int brow[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-      brow[f] = MODE == 0 ? (f < 2 ? 32 * wn + 16 * f : kTN / 2 + 32 * wn + 16 * (f - 2)) : 64 * wn + 16 * f;
     const int mfw = min(8, max(0, nmf - 8 * wm));  // valid fragments of this wave
 
     // fragments past the valid rows are skipped in halves of 4 (64 rows)
+    // per-lane LDS bases: fragment f / m then sits at a compile-time offset
+    const int off = lr * kRowSlots + (lq ^ swz(lr));
+    const int brow0 = MODE == 0 ? 32 * wn : 64 * wn;   // first B fragment row of this wave
     auto compute = [&](const i32x4_t* la, const i32x4_t* lb) {
+      const i32x4_t* pa = la + 128 * wm * kRowSlots + off;
+      const i32x4_t* pb = lb + brow0 * kRowSlots + off;
       bf16x8_t bfr[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const int row = brow[f] + lr;
-        bfr[f] = __builtin_bit_cast(bf16x8_t, lb[row * kRowSlots + (lq ^ swz(row))]);
+        const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
+        bfr[f] = __builtin_bit_cast(bf16x8_t, pb[fr * kRowSlots]);
       }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         if (mfw > 4 * hf) {
           bf16x8_t af[4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int row = 128 * wm + 16 * (4 * hf + m) + lr;
-            af[m] = __builtin_bit_cast(bf16x8_t, la[row * kRowSlots + (lq ^ swz(row))]);
-          }
+          for (int m = 0; m < 4; ++m) af[m] = __builtin_bit_cast(bf16x8_t, pa[16 * (4 * hf + m) * kRowSlots]);
 #pragma unroll
           for (int m = 0; m < 4; ++m)
 #pragma unroll

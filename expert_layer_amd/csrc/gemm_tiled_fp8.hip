@@ -1,0 +1,321 @@
+// Grouped expert GEMMs with FP8 (OCP E4M3FN) operands for large groups:
+// LDS-tiled, one v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales) per 128-wide
+// K block, whose partial sums are promoted into fp32 accumulators with the
+// row scale of the activations times the 128x128 weight-block scale
+// (GroupGEMM FP8 block-wise, HPC-Ops page, main functions; 128x128 scales,
+// PR #54160 report, implementation item 4):
+//     acc[m][n] += (xs[m, kb] * ws[n/128, kb]) * partial_kb[m][n].
+// The Gate-Up kernel fuses SwiGLU and the activation requantisation stage of
+// FusedMoE (one 128-column group of h per tile, the row amax is reduced over
+// the four column waves through LDS) and gathers its A rows through the
+// routing index.
+//
+// Tile: up to 256 rows x 256 weight rows, one 128-k block per stage (128 B
+// per row: every direct-to-LDS load instruction fills 8 whole rows), a ring
+// of 2 stages (2 x 65 KB incl. the activation scales of the stage).  Eight
+// waves in a 2 (rows) x 4 (weight rows) grid, two per SIMD, as in the bf16
+// kernels; items, the XCD-aware worker order and fragment skipping likewise.
+#include "tiles.hpp"
+
+namespace moe355 {
+
+namespace {
+
+constexpr int kTM = 256;
+constexpr int kTN = 256;
+constexpr int kTK = 128;                 // k per stage = one scale block
+constexpr int kThreads = 512;
+constexpr int kSlots = kTK / 16;         // 16-byte slots per row (8)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
+// slot of chunk c of row r: rows 2j, 2j+1 use different halves of a 256-byte
+// bank sweep and 8 consecutive rows hit 8 distinct 16-byte bank groups
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+__device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0,
+                                                         127);
+}
+
+// Fragment of 16 rows x 128 k at tile row `row0` (a multiple of 16): lane
+// (lr, lq) takes chunks lq and lq + 4 of row row0 + lr (a bijection of the
+// block's k shared by A and B).  swz8 depends on the low 4 row bits only, so
+// the per-lane slot offsets are the same for every fragment and row0 becomes
+// an immediate offset of the LDS read.
+__device__ __forceinline__ i32x8_t read_frag(const i32x4_t* plo, const i32x4_t* phi, int row0) {
+  const i32x4_t lo = plo[row0 * kSlots];
+  const i32x4_t hi = phi[row0 * kSlots];
+  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <int MODE, int YBF16>  // MODE 0: Gate-Up (+SwiGLU, requantised h); MODE 1: Down (y)
+__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const uint8_t* __restrict__ A,
+                                                              const float* __restrict__ As,
+                                                              void* __restrict__ out,
+                                                              float* __restrict__ out_s) {
+  __shared__ __attribute__((aligned(1024))) i32x4_t a0[kTM * kSlots], a1[kTM * kSlots];
+  __shared__ __attribute__((aligned(1024))) i32x4_t b0[kTN * kSlots], b1[kTN * kSlots];
+  __shared__ __attribute__((aligned(16))) float s0[kTM], s1[kTM];
+  __shared__ float red[4][kTM];
+  __shared__ ChunkTable tab;
+
+  const int G = a.E + (a.has_shared ? 1 : 0);
+  const int nmt_total = build_chunks(tab, a.offsets, G, kTM);
+  const int H = a.H, I = a.I;
+  const int K = MODE == 0 ? H : I;
+  const int KB = K / kTK;                 // k blocks
+  const int NT = MODE == 0 ? (2 * I) / kTN : H / kTN;
+  const int64_t items = (int64_t)nmt_total * NT;
+  const int64_t P = a.T * a.k;
+  const int IB = I / 128, HB = H / 128;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int lrow = lane >> 3, lslot = lane & 7;   // direct-load role: 8 rows x 8 slots per load
+  const int off_lo = lr * kSlots + (lq ^ swz8(lr)), off_hi = lr * kSlots + ((lq + 4) ^ swz8(lr));
+
+  const int nblk = gridDim.x;
+  const int per_xcd = nblk / 8;
+  const int b = blockIdx.x;
+  const int worker = (nblk % 8 == 0) ? (b % 8) * per_xcd + b / 8 : b;
+
+  for (int64_t it = worker; it < items; it += nblk) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)tab.prefix[mid] * NT <= it) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int mtg = tab.prefix[g + 1] - tab.prefix[g];
+    const int local = (int)(it - (int64_t)tab.prefix[g] * NT);
+    const int nt = local / mtg, mt = local % mtg;
+    const int cnt = a.offsets[g + 1] - a.offsets[g];
+    const int rs = mt * kTM;
+    const int nrows = min(kTM, cnt - rs);
+    const int r0 = a.offsets[g] + rs;
+    const int nmf = (nrows + 15) >> 4;
+    const bool shared = g == a.E;
+
+    // A rows: load i (0..3) of this wave fills tile rows 8*(4*wave+i) + lane/8
+    int a_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * (4 * wave + i) + lrow;
+      const int r = r0 + min(row, nrows - 1);
+      int64_t base;
+      if (MODE == 0) {
+        const int64_t t = r < P ? (int64_t)(a.slot_pair[r] / a.k) : (int64_t)r - P;
+        base = t * H;
+      } else {
+        base = (int64_t)r * I;
+      }
+      a_off[i] = (int)base + ((lslot ^ swz8(row)) * 16);
+    }
+    // activation scales of the tile rows: waves 0..3 load rows 64*wave + lane
+    int as_off = 0;
+    if (wave < 4) {
+      const int row = 64 * wave + lane;
+      const int r = r0 + min(row, nrows - 1);
+      int64_t base;
+      if (MODE == 0) {
+        const int64_t t = r < P ? (int64_t)(a.slot_pair[r] / a.k) : (int64_t)r - P;
+        base = t * (H / 128);
+      } else {
+        base = (int64_t)r * IB;
+      }
+      as_off = (int)base;
+    }
+    // B rows: same interleaving as the bf16 Gate-Up tile (rows [0,128) gate,
+    // [128,256) up of columns n0..n0+127, n0 = 128*nt)
+    const uint8_t* bw;
+    const float *wsc0, *wsc1;   // weight scales [.., KB] for the wave's gate/up (or down) columns
+    int b_off[4];
+    const int64_t mat = (int64_t)I * H;
+    if (MODE == 0) {
+      const int half = wave >> 2;  // waves 0-3 load gate rows, 4-7 up rows
+      const uint8_t* wmat = static_cast<const uint8_t*>(half == 0 ? (shared ? a.sw1 : a.w1) : (shared ? a.sw3 : a.w3));
+      bw = wmat + (shared ? 0 : g * mat) + (int64_t)(nt * (kTN / 2)) * H;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * wave + i) + lrow;        // 0..255 in the B tile
+        const int wrow = row - half * (kTN / 2);
+        b_off[i] = wrow * H + ((lslot ^ swz8(row)) * 16);
+      }
+      const int64_t blk = (int64_t)IB * HB;
+      wsc0 = (shared ? a.ss1 : a.s1 + g * blk) + (int64_t)nt * HB;
+      wsc1 = (shared ? a.ss3 : a.s3 + g * blk) + (int64_t)nt * HB;
+    } else {
+      const uint8_t* wmat = static_cast<const uint8_t*>(shared ? a.sw2 : a.w2);
+      bw = wmat + (shared ? 0 : g * mat) + (int64_t)(nt * kTN) * I;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * wave + i) + lrow;
+        b_off[i] = row * I + ((lslot ^ swz8(row)) * 16);
+      }
+      const int64_t blk = (int64_t)HB * IB;
+      wsc0 = (shared ? a.ss2 : a.s2 + g * blk) + (int64_t)(2 * nt + (wn >> 1)) * IB;
+      wsc1 = wsc0;
+    }
+
+    auto issue = [&](int kb, i32x4_t* la, i32x4_t* lb, float* ls) {
+      const int k0 = kb * kTK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        load_lds16(A + a_off[i] + k0, &la[(4 * wave + i) * 64]);
+        load_lds16(bw + b_off[i] + k0, &lb[(4 * wave + i) * 64]);
+      }
+      if (wave < 4) load_lds4(As + as_off + kb, &ls[64 * wave]);
+    };
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int mfw = min(8, max(0, nmf - 8 * wm));
+
+    // per-lane LDS bases: fragment f / m then sits at a compile-time offset
+    const int brow0 = MODE == 0 ? 32 * wn : 64 * wn;   // first B fragment row of this wave
+    auto compute = [&](int kb, const i32x4_t* la, const i32x4_t* lb, const float* ls) {
+      if (mfw == 0) return;
+      const float wg = wsc0[kb], wu = wsc1[kb];
+      const i32x4_t* alo = la + 128 * wm * kSlots + off_lo;
+      const i32x4_t* ahi = la + 128 * wm * kSlots + off_hi;
+      const i32x4_t* blo = lb + brow0 * kSlots + off_lo;
+      const i32x4_t* bhi = lb + brow0 * kSlots + off_hi;
+      const float* lsw = ls + 128 * wm + 4 * lq;
+      i32x8_t bfr[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
+        bfr[f] = read_frag(blo, bhi, fr);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m < mfw) {
+          const i32x8_t af = read_frag(alo, ahi, 16 * m);
+          const f32x4_t xs4 = *reinterpret_cast<const f32x4_t*>(&lsw[16 * m]);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const f32x4_t p = mfma_fp8(af, bfr[f]);
+            const float ws = (MODE == 0 && f >= 2) ? wu : wg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][f][i] = __builtin_fmaf(xs4[i] * ws, p[i], acc[m][f][i]);
+          }
+        }
+        // keep the partial sums of one fragment row in flight at a time (the
+        // second wave on the SIMD fills the matrix core meanwhile)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(0, a0, b0, s0);
+    // KB is even when K % 256 == 0; otherwise the loop ends after the first stage of a pair
+    for (int kb = 0; kb < KB; kb += 2) {
+      // stage kb (slot 0): its loads are the only ones in flight
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      if (kb + 1 < KB) issue(kb + 1, a1, b1, s1);
+      compute(kb, a0, b0, s0);
+      if (kb + 1 >= KB) break;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      if (kb + 2 < KB) issue(kb + 2, a0, b0, s0);
+      compute(kb + 1, a1, b1, s1);
+    }
+
+    // ---- epilogue
+    if (MODE == 0) {
+      // h = SiLU(g) * u; the tile's 128 columns are one quantisation group per row
+      uint8_t* hq = static_cast<uint8_t*>(out);
+      // h overwrites the gate accumulators (acc[m][0..1]); per-row max over this
+      // wave's 32 columns, then over the 4 column waves through LDS
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float h0 = silu_mul(acc[m][0][i], acc[m][2][i]);
+          const float h1 = silu_mul(acc[m][1][i], acc[m][3][i]);
+          acc[m][0][i] = h0;
+          acc[m][1][i] = h1;
+          const float v = wave_max16(fmaxf(fabsf(h0), fabsf(h1)));
+          if (lr == 0) red[wn][128 * wm + 16 * m + 4 * lq + i] = v;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m < mfw) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 128 * wm + 16 * m + 4 * lq + i;
+            const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
+            const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+            if (row < nrows) {
+              const int64_t r = r0 + row;
+              const int col = nt * (kTN / 2) + 32 * wn + lr;
+              hq[r * I + col] = (uint8_t)(f32x2_to_e4m3(__fdiv_rn(acc[m][0][i], sc), 0.0f) & 0xFF);
+              hq[r * I + col + 16] = (uint8_t)(f32x2_to_e4m3(__fdiv_rn(acc[m][1][i], sc), 0.0f) & 0xFF);
+              if (wn == 0 && lr == 0) out_s[r * IB + nt] = sc;
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m < mfw) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 128 * wm + 16 * m + 4 * lq + i;
+            if (row < nrows) {
+              const int64_t r = r0 + row;
+              const int col = nt * kTN + 64 * wn + lr;
+#pragma unroll
+              for (int f = 0; f < 4; ++f) {
+                if (YBF16)
+                  static_cast<uint16_t*>(out)[r * H + col + 16 * f] = (uint16_t)f32_to_bf16(acc[m][f][i]);
+                else
+                  static_cast<float*>(out)[r * H + col + 16 * f] = acc[m][f][i];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool tiled_fp8_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0; }
+bool tiled_fp8_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
+
+hipError_t launch_gemm13_fp8_tiled(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq, float* hs,
+                                   hipStream_t s) {
+  gemm_tiled_fp8<0, 0><<<device_cus(), kThreads, 0, s>>>(a, xq, xs, hq, hs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_fp8_tiled(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
+                                  hipStream_t s) {
+  if (y_dtype == 1)
+    gemm_tiled_fp8<1, 1><<<device_cus(), kThreads, 0, s>>>(a, hq, hs, y, nullptr);
+  else
+    gemm_tiled_fp8<1, 0><<<device_cus(), kThreads, 0, s>>>(a, hq, hs, y, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace moe355

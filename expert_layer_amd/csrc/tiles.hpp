@@ -73,4 +73,9 @@ __device__ inline int chunk_group(const ChunkTable& tab, int G, int c) {
   return lo;
 }
 
+// Groups of 64+ rows on average go to the LDS-tiled MFMA kernels; up to 16
+// rows on average, the weight-streaming kernels use 16-row chunks.
+inline bool large_groups(const GemmArgs& a) { return a.T * a.k >= (int64_t)a.E * 64; }
+inline bool small_groups(const GemmArgs& a) { return a.T * a.k <= (int64_t)a.E * 16; }
+
 }  // namespace moe355
