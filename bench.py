@@ -38,10 +38,14 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of every kernel source: counter figures are reported only for the sources they were taken on."""
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "gemm_fp8.hip", "tiles.hpp", "common.hpp"):
-        with open(os.path.join(ROOT, "expert_layer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "expert_layer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
