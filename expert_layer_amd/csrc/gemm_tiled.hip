@@ -8,12 +8,14 @@
 // multi-stage LDS ring instead.
 //
 // Tile: up to 256 rows of one group x 256 weight rows (Gate-Up: 128 gate +
-// 128 up columns of h; Down: 256 columns of y), 32 k per stage, a ring of 4
-// stages in LDS (128 KB, one workgroup per CU).  Stages are filled with the
-// gfx950 direct-to-LDS 16-byte loads: each load instruction writes 1 KB of
-// LDS (16 rows x 64 B) and every lane picks the global address whose 16 bytes
-// belong at its LDS slot, which realises the XOR swizzle that keeps MFMA
-// fragment reads free of bank conflicts.
+// 128 up columns of h; Down: 256 columns of y), 64 k per stage, so every row
+// of a stage is one whole 128-byte line (one L2 request per line; measured
+// faster than a deeper ring of half-line stages), a ring of 2 stages in LDS
+// (128 KB, one workgroup per CU).  Stages are filled with the gfx950
+// direct-to-LDS 16-byte loads: each load instruction writes 1 KB of LDS (8
+// rows x 128 B) and every lane picks the global address whose 16 bytes belong
+// at its LDS slot, which realises the XOR swizzle that keeps MFMA fragment
+// reads free of bank conflicts.
 //
 // Eight waves, two per SIMD, in a 2 (rows) x 4 (weight rows) grid: wave w
 // computes rows 128*(w/4) .. +127 against 64 weight rows (Gate-Up: gate
@@ -37,10 +39,11 @@ namespace {
 
 constexpr int kTM = 256;      // max rows per tile
 constexpr int kTN = 256;      // weight rows per tile
-constexpr int kTK = 32;       // k per stage
-constexpr int kStages = 4;    // LDS ring depth
+constexpr int kTK = 64;       // k per stage (one 128-byte line per row)
+constexpr int kStages = 2;    // LDS ring depth
 constexpr int kThreads = 512;  // 8 waves, two per SIMD
-constexpr int kRowSlots = kTK * 2 / 16;  // 16-byte slots per row per stage (4)
+constexpr int kRowSlots = kTK * 2 / 16;  // 16-byte slots per row per stage (8)
+constexpr int kWaitVm0 = 0xF70;          // s_waitcnt vmcnt(0) only (expcnt, lgkmcnt not waited)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
@@ -49,14 +52,12 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-// XOR swizzle of the 16-byte slot of (row, chunk) inside a 64-byte row:
-// bits (b2^b3, b1^b3) of the row.  For one chunk, rows 0..7 of either parity
-// hit distinct 16-byte bank groups of a 128-byte sweep, and rows 0..15 sharing
-// their low two bits hit distinct groups of a 256-byte sweep.  Only bits 1-3
-// are used, so every 16-row fragment shares the per-lane slot offsets.
-__device__ __forceinline__ int swz(int row) {
-  return ((((row >> 2) ^ (row >> 3)) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1);
-}
+// XOR swizzle of the 16-byte slot of (row, chunk) inside a 128-byte row: a
+// permutation of the 8 slots for rows 0..7 and for rows 8..15, and rows of
+// either parity map to distinct slots, so a 16-lane fragment read touches 16
+// distinct 16-byte bank groups.  Only bits 0-3 are used, so every 16-row
+// fragment shares the per-lane slot offsets.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -81,10 +82,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
                                                           void* __restrict__ out) {
   // one named array per ring stage: the stage being read and the stages being
   // filled are then provably distinct objects, so reads wait only for their own stage
-  __shared__ __attribute__((aligned(1024))) i32x4_t a0[kTM * kRowSlots], a1[kTM * kRowSlots],
-      a2[kTM * kRowSlots], a3[kTM * kRowSlots];
-  __shared__ __attribute__((aligned(1024))) i32x4_t b0[kTN * kRowSlots], b1[kTN * kRowSlots],
-      b2[kTN * kRowSlots], b3[kTN * kRowSlots];
+  __shared__ __attribute__((aligned(1024))) i32x4_t a0[kTM * kRowSlots], a1[kTM * kRowSlots];
+  __shared__ __attribute__((aligned(1024))) i32x4_t b0[kTN * kRowSlots], b1[kTN * kRowSlots];
   __shared__ ChunkTable tab;
 
   const int G = a.E + (a.has_shared ? 1 : 0);
@@ -100,9 +99,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-  // direct-to-LDS role: load i (0, 1) of this wave fills rows 16*(2*wave+i) + lane/4,
-  // slot lane%4 (which holds chunk slot ^ swz(row))
-  const int lrow = lane >> 2, lslot = lane & 3;
+  // direct-to-LDS role: load i (0..3) of this wave fills rows 8*(4*wave+i) + lane/8,
+  // slot lane%8 (which holds chunk slot ^ swz(row))
+  const int lrow = lane >> 3, lslot = lane & 7;
 
   // XCD-aware worker id: workgroup b runs on XCD b % 8
   const int nblk = gridDim.x;
@@ -129,10 +128,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
     const bool shared = g == a.E;
 
     // ---- per-lane global addresses for the direct-to-LDS loads (element offsets)
-    int a_off[2];
+    int a_off[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 16 * (2 * wave + i) + lrow;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * (4 * wave + i) + lrow;
       const int r = r0 + min(row, nrows - 1);
       int64_t base;
       if (MODE == 0) {
@@ -144,15 +143,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
       a_off[i] = (int)base + ((lslot ^ swz(row)) * 8);
     }
     const uint16_t* bw;   // weight rows of this wave's loads
-    int b_off[2];
+    int b_off[4];
     if (MODE == 0) {
       const int half = wave >> 2;  // waves 0-3 load gate rows, waves 4-7 up rows
       const uint16_t* wm = half == 0 ? static_cast<const uint16_t*>(shared ? a.sw1 : a.w1)
                                      : static_cast<const uint16_t*>(shared ? a.sw3 : a.w3);
       bw = wm + (shared ? 0 : (int64_t)g * I * H) + (int64_t)(nt * (kTN / 2)) * H;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = 16 * (2 * wave + i) + lrow;     // 0..255 in the B tile
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * wave + i) + lrow;      // 0..255 in the B tile
         const int wrow = row - half * (kTN / 2);        // 0..127 inside gate or up
         b_off[i] = wrow * H + ((lslot ^ swz(row)) * 8);
       }
@@ -160,8 +159,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
       const uint16_t* wm = static_cast<const uint16_t*>(shared ? a.sw2 : a.w2);
       bw = wm + (shared ? 0 : (int64_t)g * H * I) + (int64_t)(nt * kTN) * I;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = 16 * (2 * wave + i) + lrow;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * wave + i) + lrow;
         b_off[i] = row * I + ((lslot ^ swz(row)) * 8);
       }
     }
@@ -169,9 +168,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
     auto issue = [&](int kk, i32x4_t* la, i32x4_t* lb) {
       const int k0 = kk * kTK;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        load_lds16(A + a_off[i] + k0, &la[(2 * wave + i) * 64]);
-        load_lds16(bw + b_off[i] + k0, &lb[(2 * wave + i) * 64]);
+      for (int i = 0; i < 4; ++i) {
+        load_lds16(A + a_off[i] + k0, &la[(4 * wave + i) * 64]);
+        load_lds16(bw + b_off[i] + k0, &lb[(4 * wave + i) * 64]);
       }
     };
 
@@ -185,62 +184,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
 
     // fragments past the valid rows are skipped in halves of 4 (64 rows)
     // per-lane LDS bases: fragment f / m then sits at a compile-time offset
-    const int off = lr * kRowSlots + (lq ^ swz(lr));
+    const int off0 = lr * kRowSlots + (lq ^ swz(lr));        // k 0..31 of the stage
+    const int off1 = lr * kRowSlots + ((lq ^ swz(lr)) ^ 4);  // k 32..63
     const int brow0 = MODE == 0 ? 32 * wn : 64 * wn;   // first B fragment row of this wave
     auto compute = [&](const i32x4_t* la, const i32x4_t* lb) {
-      const i32x4_t* pa = la + 128 * wm * kRowSlots + off;
-      const i32x4_t* pb = lb + brow0 * kRowSlots + off;
-      bf16x8_t bfr[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
-        bfr[f] = __builtin_bit_cast(bf16x8_t, pb[fr * kRowSlots]);
-      }
+      for (int j = 0; j < 2; ++j) {
+        const i32x4_t* pa = la + 128 * wm * kRowSlots + (j ? off1 : off0);
+        const i32x4_t* pb = lb + brow0 * kRowSlots + (j ? off1 : off0);
+        bf16x8_t bfr[4];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if (mfw > 4 * hf) {
-          bf16x8_t af[4];
+        for (int f = 0; f < 4; ++f) {
+          const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
+          bfr[f] = __builtin_bit_cast(bf16x8_t, pb[fr * kRowSlots]);
+        }
 #pragma unroll
-          for (int m = 0; m < 4; ++m) af[m] = __builtin_bit_cast(bf16x8_t, pa[16 * (4 * hf + m) * kRowSlots]);
+        for (int hf = 0; hf < 2; ++hf) {
+          if (mfw > 4 * hf) {
+            bf16x8_t af[4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m) af[m] = __builtin_bit_cast(bf16x8_t, pa[16 * (4 * hf + m) * kRowSlots]);
 #pragma unroll
-            for (int f = 0; f < 4; ++f) acc[4 * hf + m][f] = mfma16(af[m], bfr[f], acc[4 * hf + m][f]);
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+              for (int f = 0; f < 4; ++f) acc[4 * hf + m][f] = mfma16(af[m], bfr[f], acc[4 * hf + m][f]);
+          }
         }
       }
     };
 
-    // one stage: wait for this stage's loads (at most `ahead` later stages stay in
-    // flight, 4 loads each), barrier, refill the stage computed last time, compute
-    auto stage = [&](int kk, const i32x4_t* la, const i32x4_t* lb, i32x4_t* fa, i32x4_t* fb) {
-      const int ahead = nk - 1 - kk;
-      if (ahead >= 2)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if (ahead == 1)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      // execution barrier only: a fence here would also wait for the stages still
-      // in flight; the vmcnt wait above already put this stage's bytes in LDS
+    // one stage: wait for this stage's loads (the only ones in flight), barrier,
+    // refill the other slot with the next stage, compute.  The waits are the
+    // compiler's s_waitcnt builtin rather than inline asm: its own wait
+    // insertion then knows that the loads and the previous item's stores are
+    // done, and adds no full drain of its own in front of the fragment reads.
+    auto stage = [&](bool refill, int kk, const i32x4_t* la, const i32x4_t* lb, i32x4_t* fa, i32x4_t* fb) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      // execution barrier only: a fence here would also wait for the stage still
+      // in flight; the wait above already put this stage's bytes in LDS
       __builtin_amdgcn_s_barrier();
-      if (kk + kStages - 1 < nk) issue(kk + kStages - 1, fa, fb);
+      if (refill) issue(kk + 1, fa, fb);
       compute(la, lb);
     };
 
     // previous item's stores retired (stores also count in vmcnt) and every wave
     // finished reading the ring before it is refilled
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    // nk = K / 64 is even (K % 128 == 0); the steady loop has no branches
     issue(0, a0, b0);
-    if (nk > 1) issue(1, a1, b1);
-    if (nk > 2) issue(2, a2, b2);
-    // nk is a multiple of 4 (K % 128 == 0)
-    for (int kk = 0; kk < nk; kk += kStages) {
-      stage(kk + 0, a0, b0, a3, b3);
-      stage(kk + 1, a1, b1, a0, b0);
-      stage(kk + 2, a2, b2, a1, b1);
-      stage(kk + 3, a3, b3, a2, b2);
+    for (int kk = 0; kk < nk - kStages; kk += kStages) {
+      stage(true, kk + 0, a0, b0, a1, b1);
+      stage(true, kk + 1, a1, b1, a0, b0);
     }
+    stage(true, nk - 2, a0, b0, a1, b1);
+    stage(false, nk - 1, a1, b1, a0, b0);
 
     // ---- epilogue
 #pragma unroll

@@ -26,6 +26,7 @@ constexpr int kTN = 256;
 constexpr int kTK = 128;                 // k per stage = one scale block
 constexpr int kThreads = 512;
 constexpr int kSlots = kTK / 16;         // 16-byte slots per row (8)
+constexpr int kWaitVm0 = 0xF70;          // s_waitcnt vmcnt(0) only (expcnt, lgkmcnt not waited)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
@@ -187,9 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
 
     // per-lane LDS bases: fragment f / m then sits at a compile-time offset
     const int brow0 = MODE == 0 ? 32 * wn : 64 * wn;   // first B fragment row of this wave
-    auto compute = [&](int kb, const i32x4_t* la, const i32x4_t* lb, const float* ls) {
+    auto compute = [&](float wg, float wu, const i32x4_t* la, const i32x4_t* lb, const float* ls) {
       if (mfw == 0) return;
-      const float wg = wsc0[kb], wu = wsc1[kb];
       const i32x4_t* alo = la + 128 * wm * kSlots + off_lo;
       const i32x4_t* ahi = la + 128 * wm * kSlots + off_hi;
       const i32x4_t* blo = lb + brow0 * kSlots + off_lo;
@@ -220,21 +220,45 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
       }
     };
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    // Weight scales of the stage being computed.  The next stage's scales are
+    // loaded before its direct loads are issued, so the wait for them never
+    // includes a whole stage in flight; they are wave-uniform and move to
+    // scalar registers after the MFMAs.  Waits are the compiler's s_waitcnt
+    // builtin, so its own wait insertion sees them and adds no drain.
+    auto uniform = [](float v) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    };
+    float wg = uniform(wsc0[0]), wu = uniform(wsc1[0]);
     issue(0, a0, b0, s0);
     // KB is even when K % 256 == 0; otherwise the loop ends after the first stage of a pair
     for (int kb = 0; kb < KB; kb += 2) {
       // stage kb (slot 0): its loads are the only ones in flight
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __builtin_amdgcn_s_barrier();
-      if (kb + 1 < KB) issue(kb + 1, a1, b1, s1);
-      compute(kb, a0, b0, s0);
+      float gn = 0.f, un = 0.f;
+      if (kb + 1 < KB) {
+        gn = wsc0[kb + 1];
+        un = wsc1[kb + 1];
+        issue(kb + 1, a1, b1, s1);
+      }
+      compute(wg, wu, a0, b0, s0);
+      wg = uniform(gn);
+      wu = uniform(un);
       if (kb + 1 >= KB) break;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __builtin_amdgcn_s_barrier();
-      if (kb + 2 < KB) issue(kb + 2, a0, b0, s0);
-      compute(kb + 1, a1, b1, s1);
+      gn = 0.f;
+      un = 0.f;
+      if (kb + 2 < KB) {
+        gn = wsc0[kb + 2];
+        un = wsc1[kb + 2];
+        issue(kb + 2, a0, b0, s0);
+      }
+      compute(wg, wu, a1, b1, s1);
+      wg = uniform(gn);
+      wu = uniform(un);
     }
 
     // ---- epilogue
