@@ -14,6 +14,7 @@ from dataclasses import dataclass
 import torch
 
 from . import (Experts, moe_align, moe_align_workspace_bytes, moe_combine, moe_gemm2, moe_gemm13,
+               moe_gemm_workspace_bytes,
                moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_route, moe_router_gemm, moe_router_split)
 
 
@@ -69,6 +70,8 @@ class Buffers:
         self.pair_slot = torch.empty(max(P, 1), **i32)
         nws = moe_align_workspace_bytes(T, E, k)
         self.align_ws = torch.empty(max(nws // 4, 1), **i32)
+        gws = moe_gemm_workspace_bytes(layer.experts, T, k)
+        self.gemm_ws = torch.empty(max(gws // 4, 1), **i32)
         if layer.fp8:
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
             self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
@@ -115,11 +118,11 @@ def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, route
         moe_quant_rows_fp8(x, b.xq, b.xs)
         ev("quant", 1)
         ev("gemm13", 0)
-        moe_gemm13(ex, b.xq, b.xs, b.offsets, b.slot_pair, T, k, b.h, b.hs)
+        moe_gemm13(ex, b.xq, b.xs, b.offsets, b.slot_pair, T, k, b.h, b.hs, ws=b.gemm_ws)
         ev("gemm13", 1)
     else:
         ev("gemm13", 0)
-        moe_gemm13(ex, x, None, b.offsets, b.slot_pair, T, k, b.h)
+        moe_gemm13(ex, x, None, b.offsets, b.slot_pair, T, k, b.h, ws=b.gemm_ws)
         ev("gemm13", 1)
     ev("gemm2", 0)
     moe_gemm2(ex, b.h, b.hs, b.offsets, T, k, b.y)

@@ -28,6 +28,7 @@ using namespace moe355;
 namespace {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;  // slot indices are int32
+constexpr size_t kGemmWsBytes = 256;              // Gate-Up round-barrier counters (8 used)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -211,15 +212,13 @@ size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k) {
   (void)ex;
   (void)T;
   (void)k;
-  return 0;
+  return kGemmWsBytes;
 }
 
 int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const int32_t* offsets,
                const int32_t* slot_pair, int64_t T, int k, void* h, float* hs, void* ws, size_t ws_bytes,
                void* stream) {
   MOE_GUARD_BEGIN
-  (void)ws;
-  (void)ws_bytes;
   int st = check_experts(ex);
   if (st != MOE_OK) return st;
   st = check_rows(ex, T, k);
@@ -233,11 +232,16 @@ int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const in
   const size_t hbytes = (size_t)R * ex->I * (fp8 ? 1 : 2);
   if (overlap(h, hbytes, x, (size_t)T * ex->H * (fp8 ? 1 : 2))) return MOE_EINVAL;
   if (fp8 && overlap(hs, (size_t)R * (ex->I / 128) * 4, h, hbytes)) return MOE_EINVAL;
+  if (ws == nullptr || ws_bytes < kGemmWsBytes) return MOE_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 3u) return MOE_EINVAL;
+  if (overlap(ws, kGemmWsBytes, h, hbytes) || overlap(ws, kGemmWsBytes, x, (size_t)T * ex->H * (fp8 ? 1 : 2)))
+    return MOE_EINVAL;
   const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
   hipStream_t s = (hipStream_t)stream;
   if (fp8)
     return device_status(launch_gemm13_fp8(a, static_cast<const uint8_t*>(x), xs, static_cast<uint8_t*>(h), hs, s));
-  return device_status(launch_gemm13_bf16(a, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), s));
+  return device_status(
+      launch_gemm13_bf16(a, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), static_cast<int*>(ws), s));
   MOE_GUARD_END
 }
 
@@ -288,7 +292,7 @@ int moe_combine(const void* y, int y_dtype, const int32_t* pair_slot, const floa
 namespace {
 
 struct FwdLayout {
-  size_t logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, xq, xs, h, hs, y, total;
+  size_t logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, gemm_ws, xq, xs, h, hs, y, total;
 };
 
 FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype, bool router) {
@@ -309,6 +313,7 @@ FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype,
   L.slot_pair = take((size_t)P * 4);
   L.pair_slot = take((size_t)P * 4);
   L.align_ws = take(moe_align_workspace_bytes(T, ex->E, k));
+  L.gemm_ws = take(kGemmWsBytes);
   L.xq = take(fp8 ? (size_t)T * ex->H : 0);
   L.xs = take(fp8 ? (size_t)T * (ex->H / 128) * 4 : 0);
   L.h = take((size_t)R * ex->I * (fp8 ? 1 : 2));
@@ -383,7 +388,7 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
     if (e != hipSuccess) return MOE_EDEVICE;
     e = launch_gemm2_fp8(a, static_cast<const uint8_t*>(h), hs, y, args->y_dtype, s);
   } else {
-    e = launch_gemm13_bf16(a, args->x, static_cast<uint16_t*>(h), s);
+    e = launch_gemm13_bf16(a, args->x, static_cast<uint16_t*>(h), reinterpret_cast<int*>(base + L.gemm_ws), s);
     if (e != hipSuccess) return MOE_EDEVICE;
     e = launch_gemm2_bf16(a, static_cast<const uint16_t*>(h), y, args->y_dtype, s);
   }

@@ -74,7 +74,8 @@ struct GemmArgs {
   const int32_t* slot_pair;  // [P]
 };
 
-hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
+// sync: 8 ints of device scratch for the tiled kernel's round barrier
+hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm13_fp8(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq,
                              float* hs, hipStream_t s);
@@ -83,7 +84,7 @@ hipError_t launch_gemm2_fp8(const GemmArgs& a, const uint8_t* hq, const float* h
 
 bool tiled_gemm13_ok(const GemmArgs& a);
 bool tiled_gemm2_ok(const GemmArgs& a);
-hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
+hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s);
 
 bool tiled_fp8_gemm13_ok(const GemmArgs& a);

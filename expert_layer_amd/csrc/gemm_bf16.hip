@@ -264,8 +264,8 @@ int stream_grid() { return device_cus() * 8; }
 
 // The K loops need K % (64 * D) == 0: D = 4 when K is a multiple of 256,
 // otherwise D = 2 (K is always a multiple of 128).
-hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
-  if (large_groups(a) && tiled_gemm13_ok(a)) return launch_gemm13_tiled(a, x, h, s);
+hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s) {
+  if (large_groups(a) && tiled_gemm13_ok(a)) return launch_gemm13_tiled(a, x, h, sync, s);
   const bool deep = a.H % 256 == 0;
   if (!small_groups(a))
     gemm13_stream<4, 2><<<stream_grid(), kThreads, 0, s>>>(a, x, h);

@@ -206,12 +206,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
         if (m < mfw) {
           const i32x8_t af = read_frag(alo, ahi, 16 * m);
           const f32x4_t xs4 = *reinterpret_cast<const f32x4_t*>(&lsw[16 * m]);
+          // the four block products first, then their promotion: each fma waits
+          // only for an MFMA issued three or more slots earlier
+          f32x4_t p[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) p[f] = mfma_fp8(af, bfr[f]);
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            const f32x4_t p = mfma_fp8(af, bfr[f]);
             const float ws = (MODE == 0 && f >= 2) ? wu : wg;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][f][i] = __builtin_fmaf(xs4[i] * ws, p[i], acc[m][f][i]);
+            for (int i = 0; i < 4; ++i) acc[m][f][i] = __builtin_fmaf(xs4[i] * ws, p[f][i], acc[m][f][i]);
           }
         }
         // keep the partial sums of one fragment row in flight at a time (the

@@ -154,7 +154,16 @@ typedef struct moe_experts_t {
  *   sums over each 128-wide K block are scaled by xs[t,kb] * s[g,n/128,kb];
  *   h is requantised per row per 128 columns into h e4m3 [R,I] and hs fp32
  *   [R,I/128] with the same rule as moe_quant_rows_fp8.
- * offsets, slot_pair: from moe_align.  ws: moe_gemm_workspace_bytes bytes.
+ * offsets, slot_pair: from moe_align.
+ * ws: device scratch of moe_gemm_workspace_bytes bytes, 4-byte aligned; its
+ *   contents need not be initialised (the call clears what it uses, on its
+ *   stream).  The bf16 kernel for large groups keeps one counter per XCD in
+ *   it, at which the workgroups of that XCD meet after every round of tiles
+ *   so that tiles sharing operands stream them through L2 together.  The
+ *   waits are bounded, so the workspace affects timing only, never results;
+ *   calls that may run concurrently should still use separate workspaces.
+ *   ws NULL or smaller than the query: MOE_EWORKSPACE; ws overlapping x or h
+ *   or misaligned: MOE_EINVAL.
  */
 size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k);
 int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const int32_t* offsets,
@@ -165,6 +174,7 @@ int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const in
  * y[s] = h[s].w2[g]^T for every slot s of group g (fp32 accumulation; fp8
  * partial sums per 128-wide K block scaled by hs[s,kb] * s2[g,n/128,kb]).
  * y is fp32 (y_dtype MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16), [R,H].
+ * ws, ws_bytes: reserved, unused (NULL and 0 are accepted).
  */
 int moe_gemm2(const moe_experts_t* ex, const void* h, const float* hs, const int32_t* offsets,
               int64_t T, int k, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream);

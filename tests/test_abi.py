@@ -108,6 +108,12 @@ def test_gemm_validation(L):
     assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, x, None, None, 0, None) == moe.MOE_EINVAL       # h aliases x
     assert g13(ctypes.byref(ok), x, None, off, sp, 0, 2, h, None, None, 0, None) == moe.MOE_OK
     assert g13(None, x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL
+    need = L.moe_gemm_workspace_bytes(ctypes.byref(ok), 4, 2)
+    assert need > 0
+    assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EWORKSPACE
+    assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, h, None, D, need - 4, None) == moe.MOE_EWORKSPACE
+    assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, h, None, D + 2, need, None) == moe.MOE_EINVAL   # misaligned
+    assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, h, None, h + 64, need, None) == moe.MOE_EINVAL  # ws inside h
     g2 = L.moe_gemm2
     assert g2(ctypes.byref(ok), h, None, off, 4, 2, x, 3, None, 0, None) == moe.MOE_EUNSUPPORTED          # y dtype
     assert g2(ctypes.byref(_experts(wtype=1, s1=A, s3=B, s2=C)), h, None, off, 4, 2, x, 0, None, 0, None) == moe.MOE_EINVAL
