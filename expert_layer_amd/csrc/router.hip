@@ -22,71 +22,137 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   lo[i] = (uint16_t)f32_to_bf16(resid * 256.0f);
 }
 
-__device__ __forceinline__ bf16x8_t ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+// Tiled router GEMM: a workgroup computes 128 tokens x 128 experts.  Per
+// stage of 64 k, the 128 token rows and the 256 weight rows (128 hi, then 128
+// lo) are one whole 128-byte line each, staged into LDS with the gfx950
+// direct-to-LDS loads (8 rows per load instruction) in a ring of 2 stages
+// (2 x 48 KB).  The activations are read once per 128 experts, the split
+// weights once per 128 tokens.  Eight waves in a 2 (tokens) x 4 (experts)
+// grid; wave (wm, wn) owns tokens 64*wm .. +63 and experts 32*wn .. +31 of
+// the tile, i.e. 4 x 2 MFMA tiles for each of hi and lo.  Rows past T or E
+// load the last valid row and are not stored.
+constexpr int kRT = 128;           // tokens per tile
+constexpr int kRE = 128;           // experts per tile
+constexpr int kRK = 64;            // k per stage
+constexpr int kRSlots = kRK * 2 / 16;  // 16-byte slots per row (8)
+constexpr int kRThreads = 512;
+constexpr int kRWaitVm0 = 0xF70;   // s_waitcnt vmcnt(0) only
 
-// A wave computes a 32-token x 64-expert tile: 2 x 4 MFMA tiles for each of
-// the hi and lo parts.  Rows past T and experts past E are masked.
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ whi,
-                                                          const uint16_t* __restrict__ wlo,
-                                                          float* __restrict__ logits, int64_t T, int H,
-                                                          int E) {
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// slot of chunk c of row r inside a 128-byte row: a permutation of the 8
+// slots for rows 0..7 and 8..15, rows of either parity on distinct slots, so
+// a 16-row fragment read hits 16 distinct 16-byte bank groups; depends on the
+// low 4 row bits only
+__device__ __forceinline__ int rswz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+__global__ __launch_bounds__(kRThreads, 1) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ whi,
+                                                                   const uint16_t* __restrict__ wlo,
+                                                                   float* __restrict__ logits, int64_t T, int H,
+                                                                   int E) {
+  __shared__ __attribute__((aligned(1024))) i32x4_t a0[kRT * kRSlots], a1[kRT * kRSlots];
+  __shared__ __attribute__((aligned(1024))) i32x4_t b0[2 * kRE * kRSlots], b1[2 * kRE * kRSlots];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-  const int ntile_e = (E + 63) / 64;
-  const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t tt = wave_id / ntile_e;
-  const int e0 = (int)(wave_id % ntile_e) * 64;
-  const int64_t t0 = tt * 32;
-  if (t0 >= T) return;
-  const bf16x8_t zero = {};
-  const uint16_t* ap[2];
+  const int lrow = lane >> 3, lslot = lane & 7;   // direct-load role: 8 rows x 8 slots per load
+  const int64_t t0 = (int64_t)blockIdx.x * kRT;
+  const int e0 = blockIdx.y * kRE;
+
+  // A: load i (0, 1) of this wave fills tile rows 8*(2*wave+i) + lane/8
+  int64_t a_off[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int64_t t = t0 + m * 16 + lr;
-    ap[m] = t < T ? x + t * H + lq * 8 : nullptr;
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (2 * wave + i) + lrow;
+    const int64_t t = min(t0 + row, T - 1);
+    a_off[i] = t * H + (lslot ^ rswz(row)) * 8;
   }
-  const uint16_t* bh[4];
-  const uint16_t* bl[4];
+  // B: load i (0..3) fills tile rows 8*(4*wave+i) + lane/8; rows [0,128) hi, [128,256) lo
+  const uint16_t* bsrc = wave < 4 ? whi : wlo;
+  int64_t b_off[4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int e = e0 + n * 16 + lr;
-    bh[n] = e < E ? whi + (int64_t)e * H + lq * 8 : nullptr;
-    bl[n] = e < E ? wlo + (int64_t)e * H + lq * 8 : nullptr;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + lrow;
+    const int e = min(e0 + (row & (kRE - 1)), E - 1);
+    b_off[i] = (int64_t)e * H + (lslot ^ rswz(row)) * 8;
   }
-  f32x4_t ah[2][4], al[2][4];
+  auto issue = [&](int kk, i32x4_t* la, i32x4_t* lb) {
+    const int k0 = kk * kRK;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int i = 0; i < 2; ++i) load_lds16(x + a_off[i] + k0, &la[(2 * wave + i) * 64]);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      ah[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      al[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) load_lds16(bsrc + b_off[i] + k0, &lb[(4 * wave + i) * 64]);
+  };
+
+  f32x4_t ah[4][2], al[4][2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      ah[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      al[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    bf16x8_t a[2], b1[4], b2[4];
+
+  // per-lane fragment bases (row lr, chunk lq or lq + 4 of the stage)
+  const int off0 = lr * kRSlots + (lq ^ rswz(lr));
+  const int off1 = lr * kRSlots + ((lq ^ rswz(lr)) ^ 4);
+  auto compute = [&](const i32x4_t* la, const i32x4_t* lb) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) a[m] = ap[m] ? ld8(ap[m] + k0) : zero;
+    for (int j = 0; j < 2; ++j) {
+      const i32x4_t* pa = la + 64 * wm * kRSlots + (j ? off1 : off0);
+      const i32x4_t* pb = lb + 32 * wn * kRSlots + (j ? off1 : off0);
+      bf16x8_t bh[2], bl[2];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      b1[n] = bh[n] ? ld8(bh[n] + k0) : zero;
-      b2[n] = bl[n] ? ld8(bl[n] + k0) : zero;
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        ah[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b1[n], ah[m][n], 0, 0, 0);
-        al[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b2[n], al[m][n], 0, 0, 0);
+      for (int f = 0; f < 2; ++f) {
+        bh[f] = __builtin_bit_cast(bf16x8_t, pb[16 * f * kRSlots]);
+        bl[f] = __builtin_bit_cast(bf16x8_t, pb[(kRE + 16 * f) * kRSlots]);
       }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, pa[16 * m * kRSlots]);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          ah[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[f], ah[m][f], 0, 0, 0);
+          al[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[f], al[m][f], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // one stage: its loads are the only ones in flight; wait, barrier, refill
+  // the other slot with the next stage, compute (builtin waits: the compiler's
+  // own wait insertion sees them)
+  auto stage = [&](bool refill, int kk, const i32x4_t* la, const i32x4_t* lb, i32x4_t* fa, i32x4_t* fb) {
+    __builtin_amdgcn_s_waitcnt(kRWaitVm0);
+    __builtin_amdgcn_s_barrier();
+    if (refill) issue(kk + 1, fa, fb);
+    compute(la, lb);
+  };
+
+  const int nk = H / kRK;   // even: H % 128 == 0
+  issue(0, a0, b0);
+  for (int kk = 0; kk < nk - 2; kk += 2) {
+    stage(true, kk, a0, b0, a1, b1);
+    stage(true, kk + 1, a1, b1, a0, b0);
   }
+  stage(true, nk - 2, a0, b0, a1, b1);
+  stage(false, nk - 1, a1, b1, a0, b0);
+
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + m * 16 + lq * 4 + i;
-        const int e = e0 + n * 16 + lr;
-        if (t < T && e < E) logits[t * E + e] = __builtin_fmaf(al[m][n][i], 0.00390625f, ah[m][n][i]);
+        const int64_t t = t0 + 64 * wm + 16 * m + 4 * lq + i;
+        const int e = e0 + 32 * wn + 16 * f + lr;
+        if (t < T && e < E) logits[t * E + e] = __builtin_fmaf(al[m][f][i], 0.00390625f, ah[m][f][i]);
       }
 }
 
@@ -99,8 +165,8 @@ hipError_t launch_router_split(const float* w, uint16_t* hi, uint16_t* lo, int64
 
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* hi, const uint16_t* lo, float* logits,
                               int64_t T, int H, int E, hipStream_t s) {
-  const int64_t waves = ((T + 31) / 32) * ((E + 63) / 64);
-  router_gemm_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(x, hi, lo, logits, T, H, E);
+  const dim3 grid((unsigned)((T + kRT - 1) / kRT), (unsigned)((E + kRE - 1) / kRE));
+  router_gemm_kernel<<<grid, kRThreads, 0, s>>>(x, hi, lo, logits, T, H, E);
   return hipGetLastError();
 }
 

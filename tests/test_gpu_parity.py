@@ -43,6 +43,8 @@ SMALL = [
     W("zipf-bias", T=200, H=256, E=32, k=8, I=128, shared=1, bias="all", seed=18),
     W("mixed-bias", T=200, H=256, E=32, k=8, I=128, shared=1, bias="mix", bias_frac=0.3, seed=19),
     W("router-small", T=100, H=512, E=64, k=8, I=128, shared=1, router=True, bias="mix", bias_frac=0.3, seed=20),
+    # router tiles of 128 tokens x 128 experts: ragged in both, two expert tiles
+    W("router-ragged", T=300, H=384, E=200, k=8, I=128, shared=1, router=True, bias="mix", bias_frac=0.3, seed=21),
 ]
 
 
