@@ -1,10 +1,15 @@
 """Benchmark of the fused MoE layer forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|router|tiny]
+                    [--launch graph|eager]
 
 A step is one pass of the whole chain (route -> align -> [quant] -> Gate-Up ->
 Down -> combine; router GEMM first for the router workload) over one batch of
-seeded synthetic input already resident in HBM.  Prints ONE JSON line.
+seeded synthetic input already resident in HBM.  The timed steps are eager
+launches on one stream with nothing else in between (with --launch graph the
+chain is captured once as a HIP graph and every step is one replay; on
+MI355X that measured no faster).  A separate pass with HIP events around
+every stage gives the per-kernel times.  Prints ONE JSON line.
 
 value = tokens per second of the whole layer (T tokens per step).  The
 roofline object describes the dominant kernel (the Gate-Up GEMM): its
@@ -140,6 +145,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="time the chain as eager launches (default) or as one captured HIP graph per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, run a plain device copy of BYTES bytes 5 times (used to scale "
@@ -192,23 +199,45 @@ def main():
     torch.cuda.synchronize()
     counts = b.counts.cpu().numpy()
 
+    # per-stage times: eager launches with events around every stage
     ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
           for _ in range(args.steps)]
+    log(f"[bench] per-stage pass, {args.steps} steps")
+    for i in range(args.steps):
+        run_chain(layer, b, d["x"], wl.k, stages=ev[i], **kw)
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in ev])) for n in names}
+
+    # whole-chain steps: eager launches, or the chain captured once as a HIP
+    # graph and replayed (the kernels and buffers are the same)
+    if args.launch == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run_chain(layer, b, d["x"], wl.k, **kw)
+        stream.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_chain(layer, b, d["x"], wl.k, **kw)
+        graph.replay()
+        step = graph.replay
+    else:
+        def step():
+            run_chain(layer, b, d["x"], wl.k, **kw)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {args.steps} steps ({args.launch})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        run_chain(layer, b, d["x"], wl.k, stages=ev[i], **kw)
+    for _ in range(args.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in ev])) for n in names}
     log("[bench] per-stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()) +
-        f"; step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms)")
+        f"; step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms, {args.launch})")
 
     value = wl.T / (ms_step * 1e-3)
     g13_bytes, g13_flops, touched = gemm13_algorithmic(wl, counts)
@@ -248,7 +277,8 @@ def main():
            "dtype": "fp8" if fp8 else "bf16", "data": "synthetic",
            "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
                       "shared": wl.shared, "weights": wl.wtype, "router": wl.router,
-                      "y_dtype": "f32" if y_dtype == torch.float32 else "bf16", "seed": wl.seed},
+                      "y_dtype": "f32" if y_dtype == torch.float32 else "bf16", "seed": wl.seed,
+                      "launch": args.launch},
            "roofline": roof, "layer": layer_info, "cpu_baseline": cpu,
            "kernel_source_hash": src_hash}
     print(json.dumps(rec), flush=True)

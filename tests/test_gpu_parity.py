@@ -15,6 +15,8 @@ import torch
 import workloads
 from gpu_helpers import check_layer, log, run_gpu
 
+from expert_layer_amd.chain import run_chain
+
 pytestmark = pytest.mark.gpu
 
 W = workloads.Workload
@@ -101,7 +103,14 @@ def test_determinism_and_forward_entry_point():
     _, b2, _ = run_gpu(wl, d)
     for name in ("ids", "w", "counts", "offsets", "slot_pair", "pair_slot", "h", "y", "out"):
         assert torch.equal(getattr(b1, name), getattr(b2, name)), name
-    layer, _, _ = run_gpu(wl, d)
+    # the same buffers again: the Gate-Up workspace still holds the previous
+    # call's round counters, which the call must clear before use
+    layer, b3, _ = run_gpu(wl, d)
+    first = b3.out.clone()
+    run_chain(layer, b3, d["x"], wl.k, logits=d["logits"], bias=d["bias"], bias_rows=d["bias_rows"])
+    torch.cuda.synchronize()
+    assert torch.equal(b3.out, first)
+    assert torch.equal(first, b1.out)
     ws = torch.empty(moe.moe_forward_workspace_bytes(layer.experts, wl.T, wl.k), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
@@ -166,3 +175,34 @@ def test_layer_configs(name, ydt):
     check_layer(wl, d, y_dtype=ydt)
     del d
     _free()
+
+
+@pytest.mark.parametrize("shape", ["streaming", "tiled"])
+def test_graph_replay_matches_eager(shape):
+    """The chain captured as a HIP graph: every replay, with eager launches and
+    synchronisations between replays, gives the eager result bit for bit."""
+    if shape == "streaming":
+        wl = W("graph-s", T=64, H=512, E=64, k=8, I=256, shared=1, seed=41)
+    else:
+        wl = W("graph-t", T=500, H=512, E=32, k=8, I=256, shared=1, bias="mix", bias_frac=0.3, seed=42)
+    d = _inputs(wl)
+    layer, b, _ = run_gpu(wl, d)
+    want = b.out.clone()
+    kw = dict(logits=d["logits"], bias=d["bias"], bias_rows=d["bias_rows"])
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run_chain(layer, b, d["x"], wl.k, **kw)
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_chain(layer, b, d["x"], wl.k, **kw)
+    for i in range(3):
+        b.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.out, want), f"replay {i}"
+        run_chain(layer, b, d["x"], wl.k, **kw)     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(b.out, want), f"eager after replay {i}"
