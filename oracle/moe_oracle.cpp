@@ -30,6 +30,13 @@
 //    code = encode(fp32(v / scale)).
 //  * router split: hi = bf16_rne(w), lo = bf16_rne((w - hi) * 256),
 //    logits = acc_hi + acc_lo / 256.
+//  * MXFP8 (the microscaling FP8 format the PR report lists beside the
+//    128x128 blockwise scales): blocks of 32 consecutive values along the
+//    reduction dimension share a power-of-two scale 2^X stored as an E8M0
+//    byte X + 127; X = floor(log2(amax)) - 8 (8 = exponent of E4M3's largest
+//    power of two), clamped to [-127, 127]; an all-zero block uses X = -127;
+//    elements are E4M3FN codes of v * 2^-X, rounded to nearest even and
+//    saturated at 448.
 //
 // Parity pins for every function here live in tests/test_oracle_*.py.
 
@@ -103,6 +110,23 @@ uint8_t e4m3_code(float v) {
 
 double silu(double z) { return z / (1.0 + std::exp(-z)); }
 
+// MX shared exponent of a block with largest magnitude amax (finite, >= 0).
+int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = 0;
+  std::frexp(amax, &e);   // amax = m * 2^e, 0.5 <= m < 1, so floor(log2(amax)) = e - 1
+  return std::min(127, std::max(-127, e - 1 - 8));
+}
+
+// One MX block of n values: scale byte and E4M3 codes of v * 2^-X.
+void mx_quant_block(const float* v, int n, uint8_t* q, uint8_t* sbyte) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) amax = std::max(amax, std::fabs(v[i]));
+  const int X = mx_exponent(amax);
+  *sbyte = static_cast<uint8_t>(X + 127);
+  for (int i = 0; i < n; ++i) q[i] = e4m3_code(static_cast<float>(std::ldexp(static_cast<double>(v[i]), -X)));
+}
+
 template <class F>
 void parallel_for(int64_t n, int nthreads, F f) {
   if (nthreads <= 1 || n <= 1) {
@@ -130,6 +154,29 @@ uint8_t orc_e4m3_code(float v) { return e4m3_code(v); }
 
 void orc_e4m3_code_array(const float* v, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = e4m3_code(v[i]);
+}
+
+int orc_mx_exponent(float amax) { return mx_exponent(amax); }
+
+// MXFP8 quantisation of rows of bf16 values (activations, or weight rows with
+// K along the columns): per row, per 32 consecutive columns, one E8M0 scale
+// byte s[r, c/32] and the codes q[r, c].
+void orc_quant_rows_mx(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* s, int nthreads) {
+  const int nb = cols / 32;
+  parallel_for(rows, nthreads, [&](int64_t r) {
+    float v[32];
+    for (int b = 0; b < nb; ++b) {
+      for (int i = 0; i < 32; ++i) v[i] = static_cast<float>(bf16_value(x[r * cols + b * 32 + i]));
+      mx_quant_block(v, 32, q + r * cols + b * 32, s + r * nb + b);
+    }
+  });
+}
+
+// The same rule on fp32 rows (the requantisation of h).
+void orc_quant_rows_mx_f32(const float* x, int64_t rows, int cols, uint8_t* q, uint8_t* s) {
+  const int nb = cols / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int b = 0; b < nb; ++b) mx_quant_block(x + r * cols + b * 32, 32, q + r * cols + b * 32, s + r * nb + b);
 }
 
 // ---------------------------------------------------------------- router
@@ -301,6 +348,20 @@ static double fp8_dot(const uint8_t* xq, const float* xs, const uint8_t* wq, con
   return acc;
 }
 
+// MXFP8 dot product of one activation row with one weight row: sum over
+// 32-wide K blocks of 2^(Xa + Xb) * sum_k dec(xq[k]) * dec(wq[k]), with the
+// scale bytes xs[b] = Xa + 127 and ws[b] = Xb + 127.
+static double mx_dot(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, int K) {
+  const double* dec = e4m3_table();
+  double acc = 0.0;
+  for (int b = 0; b < K / 32; ++b) {
+    double part = 0.0;
+    for (int i = 0; i < 32; ++i) part += dec[xq[b * 32 + i]] * dec[wq[b * 32 + i]];
+    acc += std::ldexp(part, (static_cast<int>(xs[b]) - 127) + (static_cast<int>(ws[b]) - 127));
+  }
+  return acc;
+}
+
 // One SwiGLU expert on one token with FP8 operands (the "activation
 // quantisation" stage of FusedMoE between Gate-Up and Down):
 //  xq [H] e4m3 + xs [H/128]; w1q, w3q [I, H] e4m3 + s1, s3 [I/128, H/128];
@@ -339,27 +400,31 @@ void orc_expert_fp8(const uint8_t* xq, const float* xs, const uint8_t* w1q, cons
 }
 
 // ---------------------------------------------------------------- layer
-// Expert weights for the layer.  bf16 weights (wtype 0) or e4m3 codes with
-// 128x128 fp32 block scales (wtype 1).  Routed experts are [E, ...]; the
+// Expert weights for the layer.  bf16 weights (wtype 0), e4m3 codes with
+// 128x128 fp32 block scales (wtype 1: s1, s3 [E, I/128, H/128], s2
+// [E, H/128, I/128]) or MXFP8 (wtype 2: E8M0 bytes per weight row per 32 K,
+// s1, s3 [E, I, H/32], s2 [E, H, I/32]).  Routed experts are [E, ...]; the
 // shared expert (has_shared) is a single expert of the same shape.
 struct orc_layer {
   int wtype, E, H, I, has_shared;
   const void *w1, *w3, *w2;
-  const float *s1, *s3, *s2;
+  const void *s1, *s3, *s2;
   const void *sw1, *sw3, *sw2;
-  const float *ss1, *ss3, *ss2;
+  const void *ss1, *ss3, *ss2;
 };
 
 // The whole layer on a list of tokens ("top-k weighted combine", stage 5):
 //   out[r] = sum_j w[t,j] * FFN_{ids[t,j]}(x_t) + FFN_shared(x_t),  t = rows[r].
 // bf16 path: x is bf16 [T,H] and xs is NULL.  fp8 path: x is the e4m3 code
-// array [T,H] and xs [T,H/128] its scales (from orc_quant_rows_fp8).
+// array [T,H] and xs [T,H/128] its fp32 scales (from orc_quant_rows_fp8).
+// MXFP8 path: x codes [T,H] and xs [T,H/32] E8M0 bytes (orc_quant_rows_mx);
+// h is requantised per row per 32 columns with the MX rule.
 // ids / weights are the route output [T,k].  out: [nrows, H] double.
 //
 // The arithmetic per (token, expert) is exactly orc_expert_bf16 /
 // orc_expert_fp8; the loops only run expert by expert so that each expert's
 // weight rows are read once for all the checked tokens that use it.
-void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const int32_t* ids,
+void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int32_t* ids,
                     const double* weights, int k, const int64_t* rows, int64_t nrows, double* out,
                     int nthreads) {
   const int H = L->H, I = L->I, E = L->E;
@@ -369,6 +434,10 @@ void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const in
   const int per_row = k + (L->has_shared ? 1 : 0);
   const int64_t npairs = nrows * per_row;
   const bool fp8 = L->wtype != 0;
+  const bool mx = L->wtype == 2;
+  const int hm = H / 32, im = I / 32;   // MX blocks per row
+  auto fs = [](const void* p) { return static_cast<const float*>(p); };
+  auto bs = [](const void* p) { return static_cast<const uint8_t*>(p); };
 
   // pair q = r * per_row + j: token rows[r], expert ids[t,j] (j < k) or the
   // shared expert (group E, j == k)
@@ -382,7 +451,8 @@ void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const in
 
   std::vector<double> hbuf(npairs * (int64_t)I);   // h per pair (double; fp8: fp32-rounded)
   std::vector<uint8_t> hq(fp8 ? npairs * (int64_t)I : 0);
-  std::vector<float> hs(fp8 ? npairs * (int64_t)ib : 0);
+  std::vector<float> hs(fp8 && !mx ? npairs * (int64_t)ib : 0);
+  std::vector<uint8_t> hsm(mx ? npairs * (int64_t)im : 0);
   std::vector<double> ybuf(npairs * (int64_t)H);
 
   // phase 1: h = SiLU(x.w1^T) * (x.w3^T) for every pair, task = (group, 128 rows of w1/w3)
@@ -410,21 +480,37 @@ void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const in
           hbuf[q * I + n] = silu(gv) * uv;
         } else {
           const uint8_t* xr = static_cast<const uint8_t*>(x) + t * H;
-          const float* xsr = xs + t * hb;
           const uint8_t* w1 = (sh ? static_cast<const uint8_t*>(L->sw1) : static_cast<const uint8_t*>(L->w1) + g * mat) + (int64_t)n * H;
           const uint8_t* w3 = (sh ? static_cast<const uint8_t*>(L->sw3) : static_cast<const uint8_t*>(L->w3) + g * mat) + (int64_t)n * H;
-          const float* s1 = (sh ? L->ss1 : L->s1 + g * blk) + (n / 128) * hb;
-          const float* s3 = (sh ? L->ss3 : L->s3 + g * blk) + (n / 128) * hb;
-          gv = fp8_dot(xr, xsr, w1, s1, H);
-          uv = fp8_dot(xr, xsr, w3, s3, H);
+          if (mx) {
+            const uint8_t* xsr = bs(xs) + t * hm;
+            const uint8_t* s1 = sh ? bs(L->ss1) + (int64_t)n * hm : bs(L->s1) + ((int64_t)g * I + n) * hm;
+            const uint8_t* s3 = sh ? bs(L->ss3) + (int64_t)n * hm : bs(L->s3) + ((int64_t)g * I + n) * hm;
+            gv = mx_dot(xr, xsr, w1, s1, H);
+            uv = mx_dot(xr, xsr, w3, s3, H);
+          } else {
+            const float* xsr = fs(xs) + t * hb;
+            const float* s1 = (sh ? fs(L->ss1) : fs(L->s1) + g * blk) + (n / 128) * hb;
+            const float* s3 = (sh ? fs(L->ss3) : fs(L->s3) + g * blk) + (n / 128) * hb;
+            gv = fp8_dot(xr, xsr, w1, s1, H);
+            uv = fp8_dot(xr, xsr, w3, s3, H);
+          }
           hbuf[q * I + n] = static_cast<float>(silu(gv) * uv);
         }
       }
     }
   });
 
+  // MXFP8: requantise each pair's fp32-rounded h per 32 columns (MX rule)
+  if (mx) {
+    parallel_for(npairs, nthreads, [&](int64_t q) {
+      std::vector<float> hv(I);
+      for (int i = 0; i < I; ++i) hv[i] = static_cast<float>(hbuf[q * I + i]);
+      for (int b = 0; b < im; ++b) mx_quant_block(hv.data() + b * 32, 32, &hq[q * I + b * 32], &hsm[q * im + b]);
+    });
+  }
   // fp8: requantise each pair's h per 128 columns (scale amax/448)
-  if (fp8) {
+  if (fp8 && !mx) {
     parallel_for(npairs, nthreads, [&](int64_t q) {
       for (int gi = 0; gi < ib; ++gi) {
         float amax = 0.0f;
@@ -452,8 +538,13 @@ void orc_layer_rows(const orc_layer* L, const void* x, const float* xs, const in
           for (int n = 0; n < I; ++n) acc += hbuf[q * I + n] * bf16_value(w2[n]);
         } else {
           const uint8_t* w2 = (sh ? static_cast<const uint8_t*>(L->sw2) : static_cast<const uint8_t*>(L->w2) + g * mat) + (int64_t)m * I;
-          const float* s2 = (sh ? L->ss2 : L->s2 + g * blk) + (m / 128) * ib;
-          acc = fp8_dot(hq.data() + q * I, hs.data() + q * ib, w2, s2, I);
+          if (mx) {
+            const uint8_t* s2 = sh ? bs(L->ss2) + (int64_t)m * im : bs(L->s2) + ((int64_t)g * H + m) * im;
+            acc = mx_dot(hq.data() + q * I, hsm.data() + q * im, w2, s2, I);
+          } else {
+            const float* s2 = (sh ? fs(L->ss2) : fs(L->s2) + g * blk) + (m / 128) * ib;
+            acc = fp8_dot(hq.data() + q * I, hs.data() + q * ib, w2, s2, I);
+          }
         }
         ybuf[q * H + m] = acc;
       }

@@ -65,6 +65,10 @@ def lib():
         L.orc_route.argtypes = [_P, _P, _P, _I64, _I32, _I32, _P, _P]
         L.orc_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
         L.orc_quant_rows_fp8.argtypes = [_P, _I64, _I32, _P, _P]
+        L.orc_mx_exponent.restype = ctypes.c_int
+        L.orc_mx_exponent.argtypes = [ctypes.c_float]
+        L.orc_quant_rows_mx.argtypes = [_P, _I64, _I32, _P, _P, _I32]
+        L.orc_quant_rows_mx_f32.argtypes = [_P, _I64, _I32, _P, _P]
         L.orc_quant_blocks_fp8.argtypes = [_P, _I64, _I32, _I32, _P, _P, _I32]
         L.orc_expert_bf16.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_expert_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P]
@@ -156,6 +160,32 @@ def quant_rows_fp8(x_bits):
     return q, s
 
 
+def mx_exponent(amax: float) -> int:
+    """Shared exponent X of an MXFP8 block whose largest magnitude is amax."""
+    return lib().orc_mx_exponent(float(amax))
+
+
+def quant_rows_mx(x_bits, nthreads=None):
+    """MXFP8 of bf16 rows [..., cols]: codes (same shape) and E8M0 bytes [..., cols/32]."""
+    x_bits = _c(x_bits, np.uint16)
+    cols = x_bits.shape[-1]
+    rows = x_bits.size // cols
+    q = np.empty(x_bits.shape, np.uint8)
+    s = np.empty(x_bits.shape[:-1] + (cols // 32,), np.uint8)
+    lib().orc_quant_rows_mx(_ptr(x_bits), rows, cols, _ptr(q), _ptr(s), nthreads or default_threads())
+    return q, s
+
+
+def quant_rows_mx_f32(x):
+    """The same MXFP8 rule on fp32 rows."""
+    x = _c(x, np.float32)
+    cols = x.shape[-1]
+    q = np.empty(x.shape, np.uint8)
+    s = np.empty(x.shape[:-1] + (cols // 32,), np.uint8)
+    lib().orc_quant_rows_mx_f32(_ptr(x), x.size // cols, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
 def quant_blocks_fp8(w_bits, nthreads=None):
     """w_bits: [mats, rows, cols] (or [rows, cols]) bf16 bit patterns."""
     w_bits = _c(w_bits, np.uint16)
@@ -197,6 +227,8 @@ class Layer:
     w1, w3 [E, I, H], w2 [E, H, I] and the shared expert [I, H] / [H, I].
     fp8: pass ``wtype=1`` plus uint8 codes and the fp32 block scales
     s1, s3 [E, I/128, H/128], s2 [E, H/128, I/128] (and ss1/ss3/ss2).
+    MXFP8: ``wtype=2``, uint8 codes and uint8 E8M0 scales per weight row per
+    32 K: s1, s3 [E, I, H/32], s2 [E, H, I/32] (and the shared ones).
     """
 
     def __init__(self, w1, w3, w2, sw1=None, sw3=None, sw2=None, wtype=0,
@@ -205,8 +237,9 @@ class Layer:
         self.arrays = {}
         for name, a in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
             self.arrays[name] = None if a is None else _c(a, dt)
+        sdt = np.uint8 if wtype == 2 else np.float32
         for name, a in (("s1", s1), ("s3", s3), ("s2", s2), ("ss1", ss1), ("ss3", ss3), ("ss2", ss2)):
-            self.arrays[name] = None if a is None else _c(a, np.float32)
+            self.arrays[name] = None if a is None else _c(a, sdt)
         E, I, H = self.arrays["w1"].shape
         self.E, self.I, self.H, self.wtype = E, I, H, wtype
         self.has_shared = sw1 is not None
@@ -220,7 +253,7 @@ def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None):
     """out[r] = sum_j w[t,j] FFN_{ids[t,j]}(x_t) + FFN_shared(x_t) for t = rows[r] (double)."""
     dt = np.uint16 if layer.wtype == 0 else np.uint8
     x = _c(x, dt)
-    xs = None if xs is None else _c(xs, np.float32)
+    xs = None if xs is None else _c(xs, np.uint8 if layer.wtype == 2 else np.float32)
     ids = _c(ids, np.int32)
     weights = _c(weights, np.float64)
     rows = _c(rows, np.int64)
