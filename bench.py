@@ -1,6 +1,6 @@
 """Benchmark of the fused MoE layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|router|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|mxfp8|router|tiny]
                     [--launch graph|eager]
 
 A step is one pass of the whole chain (route -> align -> [quant] -> Gate-Up ->
@@ -59,15 +59,19 @@ def gemm13_algorithmic(wl, counts):
 
     bytes: w1 + w3 of every expert with at least one row (plus the shared
     expert), one read of each gathered x row per slot, one write of h per slot
-    (fp8: codes + per-128 scales).  flops: 4*H*I per slot row.
+    (fp8: codes + per-128 scales; mxfp8: codes + one scale byte per 32).
+    flops: 4*H*I per slot row.
     """
     R = wl.T * wl.k + wl.shared * wl.T
-    wb = 1 if wl.wtype == "fp8" else 2
+    wb = 1 if wl.wtype in ("fp8", "mxfp8") else 2
     touched = int((counts > 0).sum()) + wl.shared
     weight = touched * 2 * wl.I * wl.H * wb
     if wl.wtype == "fp8":
         weight += touched * 2 * (wl.I // 128) * (wl.H // 128) * 4
         act = R * (wl.H + wl.H // 128 * 4) + R * (wl.I + wl.I // 128 * 4)
+    elif wl.wtype == "mxfp8":
+        weight += touched * 2 * wl.I * (wl.H // 32)
+        act = R * (wl.H + wl.H // 32) + R * (wl.I + wl.I // 32)
     else:
         act = R * wl.H * 2 + R * wl.I * 2
     flops = 4.0 * wl.H * wl.I * R
@@ -82,11 +86,13 @@ def layer_flops(wl):
 
 
 def layer_floor_bytes(wl, counts):
-    wb = 1 if wl.wtype == "fp8" else 2
+    wb = 1 if wl.wtype in ("fp8", "mxfp8") else 2
     touched = int((counts > 0).sum()) + wl.shared
     b = touched * 3 * wl.I * wl.H * wb
     if wl.wtype == "fp8":
         b += touched * 3 * (wl.I // 128) * (wl.H // 128) * 4
+    elif wl.wtype == "mxfp8":
+        b += touched * 3 * wl.I * (wl.H // 32)
     b += wl.T * wl.H * 2 * 2  # x in, out
     b += wl.T * wl.E * 4 if not wl.router else wl.E * wl.H * 4
     return b
@@ -113,7 +119,7 @@ def cpu_baseline(wl, d, b, budget_s):
     logits = workloads.bits(d["logits"]) if not wl.router else workloads.bits(b.logits)
     bias = workloads.bits(d["bias"]) if d["bias"] is not None else None
     bias_rows = workloads.bits(d["bias_rows"]) if d["bias_rows"] is not None else None
-    if wl.wtype == "fp8":
+    if wl.wtype in ("fp8", "mxfp8"):
         return None
     L = orc.Layer(*(workloads.bits(d[n]) if d[n] is not None else None
                     for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")))
@@ -176,8 +182,9 @@ def main():
     torch.cuda.set_device(dev)
     log(f"[bench] workload {wl.name}: generating inputs")
     d = workloads.make_inputs(wl, device=dev)
-    fp8 = wl.wtype == "fp8"
-    layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=fp8)
+    fp8 = wl.wtype in ("fp8", "mxfp8")
+    layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=wl.wtype == "fp8",
+                               mx=wl.wtype == "mxfp8")
     y_dtype = torch.float32 if wl.T * (wl.k + wl.shared) * wl.H <= (1 << 24) else torch.bfloat16
     b = Buffers(layer, wl.T, wl.k, y_dtype=y_dtype, router=wl.router)
     hi = lo = None

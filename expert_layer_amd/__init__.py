@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("MOE355_LIB") or os.path.join(_PKG, "libmoe355.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EDEVICE = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
-MOE_W_BF16, MOE_W_FP8 = 0, 1
+MOE_W_BF16, MOE_W_FP8, MOE_W_MXFP8 = 0, 1, 2
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -56,6 +56,7 @@ _SIGS = {
     "moe_align": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_quant_rows_fp8": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "moe_quant_blocks_fp8": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_quant_rows_mxfp8": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(moe_experts_t), _I64, _I32]),
     "moe_gemm13": (_I32, [ctypes.POINTER(moe_experts_t), _P, _P, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "moe_gemm2": (_I32, [ctypes.POINTER(moe_experts_t), _P, _P, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]),
@@ -183,6 +184,15 @@ def moe_quant_blocks_fp8(w, q, s):
            "moe_quant_blocks_fp8")
 
 
+def moe_quant_rows_mxfp8(x, q, s):
+    """MXFP8 of bf16 rows: x [..., cols] -> codes q (same shape, uint8), E8M0 bytes s [..., cols/32]."""
+    _expect(x, torch.bfloat16, "x")
+    _expect(s, torch.uint8, "s")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    _check(lib().moe_quant_rows_mxfp8(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(x)), "moe_quant_rows_mxfp8")
+
+
 # ------------------------------------------------------------------ experts
 class Experts:
     """Holds the tensors of a layer's experts and the matching moe_experts_t.
@@ -190,6 +200,8 @@ class Experts:
     bf16: w1, w3 [E,I,H], w2 [E,H,I] (torch.bfloat16), shared sw1, sw3 [I,H], sw2 [H,I] or None.
     fp8:  the same shapes as uint8 / float8_e4m3fn codes plus fp32 block scales
           s1, s3 [E,I/128,H/128], s2 [E,H/128,I/128] (ss1, ss3, ss2 for the shared expert).
+    mxfp8: codes plus uint8 E8M0 scales per weight row per 32 K: s1, s3 [E,I,H/32],
+          s2 [E,H,I/32] (the scale dtype selects the format).
     """
 
     def __init__(self, w1, w3, w2, sw1=None, sw3=None, sw2=None, s1=None, s3=None, s2=None,
@@ -200,7 +212,8 @@ class Experts:
         E, I, H = w1.shape
         self.E, self.I, self.H = E, I, H
         self.has_shared = int(sw1 is not None)
-        self.wtype = MOE_W_FP8 if fp8 else MOE_W_BF16
+        mx = fp8 and s1 is not None and s1.dtype == torch.uint8
+        self.wtype = MOE_W_MXFP8 if mx else MOE_W_FP8 if fp8 else MOE_W_BF16
         p = {n: _ptr(t) for n, t in self.tensors.items()}
         self.c = moe_experts_t(self.wtype, E, H, I, self.has_shared,
                                p["w1"], p["w3"], p["w2"], p["s1"], p["s3"], p["s2"],

@@ -15,22 +15,39 @@ import torch
 
 from . import (Experts, moe_align, moe_align_workspace_bytes, moe_combine, moe_gemm2, moe_gemm13,
                moe_gemm_workspace_bytes,
-               moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_route, moe_router_gemm, moe_router_split)
+               moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_quant_rows_mxfp8, moe_route, moe_router_gemm,
+               moe_router_split)
 
 
 @dataclass
 class Layer:
     experts: Experts
-    fp8: bool
+    fp8: bool          # e4m3 codes (128x128 fp32 scales, or MXFP8 when mx)
     E: int
     H: int
     I: int
     shared: int
+    mx: bool = False   # MXFP8: E8M0 scales per 32 K
 
     @staticmethod
-    def from_weights(w1, w3, w2, sw1=None, sw3=None, sw2=None, fp8=False):
-        """bf16 weights as given; fp8 quantises them once with 128x128 block scales."""
+    def from_weights(w1, w3, w2, sw1=None, sw3=None, sw2=None, fp8=False, mx=False):
+        """bf16 weights as given; fp8 quantises them once with 128x128 block
+        scales, mx once with MXFP8 (per weight row per 32 K)."""
         E, I, H = w1.shape
+        if mx:
+            q = {}
+            for name, w in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
+                if w is None:
+                    q[name] = (None, None)
+                    continue
+                cols = w.shape[-1]
+                qt = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+                st = torch.empty(w.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=w.device)
+                moe_quant_rows_mxfp8(w.contiguous(), qt, st)
+                q[name] = (qt, st)
+            ex = Experts(*(q[n][0] for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")),
+                         *(q[n][1] for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")))
+            return Layer(ex, True, E, H, I, int(sw1 is not None), mx=True)
         if not fp8:
             ex = Experts(w1, w3, w2, sw1, sw3, sw2)
             return Layer(ex, False, E, H, I, int(sw1 is not None))
@@ -72,7 +89,12 @@ class Buffers:
         self.align_ws = torch.empty(max(nws // 4, 1), **i32)
         gws = moe_gemm_workspace_bytes(layer.experts, T, k)
         self.gemm_ws = torch.empty(max(gws // 4, 1), **i32)
-        if layer.fp8:
+        if layer.mx:
+            self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+            self.h = torch.empty((R, I), dtype=torch.uint8, device=dev)
+            self.hs = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+        elif layer.fp8:
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
             self.xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
             self.h = torch.empty((R, I), dtype=torch.uint8, device=dev)
@@ -115,7 +137,10 @@ def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, route
     ex = layer.experts
     if layer.fp8:
         ev("quant", 0)
-        moe_quant_rows_fp8(x, b.xq, b.xs)
+        if layer.mx:
+            moe_quant_rows_mxfp8(x, b.xq, b.xs)
+        else:
+            moe_quant_rows_fp8(x, b.xq, b.xs)
         ev("quant", 1)
         ev("gemm13", 0)
         moe_gemm13(ex, b.xq, b.xs, b.offsets, b.slot_pair, T, k, b.h, b.hs, ws=b.gemm_ws)

@@ -51,17 +51,24 @@ int check_route_shape(int64_t T, int E, int k) {
 
 int check_experts(const moe_experts_t* ex) {
   if (ex == nullptr) return MOE_EINVAL;
-  if (ex->wtype != MOE_W_BF16 && ex->wtype != MOE_W_FP8) return MOE_EUNSUPPORTED;
+  if (ex->wtype != MOE_W_BF16 && ex->wtype != MOE_W_FP8 && ex->wtype != MOE_W_MXFP8) return MOE_EUNSUPPORTED;
   if (ex->E <= 0 || ex->H <= 0 || ex->I <= 0) return MOE_EINVAL;
   if (ex->has_shared != 0 && ex->has_shared != 1) return MOE_EINVAL;
   if (ex->E > 1024 || ex->H % 128 != 0 || ex->I % 128 != 0) return MOE_EUNSUPPORTED;
   if (!ex->w1 || !ex->w3 || !ex->w2) return MOE_EINVAL;
   if (!aligned16(ex->w1) || !aligned16(ex->w3) || !aligned16(ex->w2)) return MOE_EINVAL;
-  if (ex->wtype == MOE_W_FP8 && (!ex->s1 || !ex->s3 || !ex->s2)) return MOE_EINVAL;
+  const bool scaled = ex->wtype != MOE_W_BF16;
+  if (scaled && (!ex->s1 || !ex->s3 || !ex->s2)) return MOE_EINVAL;
+  // the MXFP8 Down kernel tiles 256 output columns; its scale rows are read
+  // as 4-byte words
+  auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (ex->wtype == MOE_W_MXFP8 && ex->H % 256 != 0) return MOE_EUNSUPPORTED;
+  if (ex->wtype == MOE_W_MXFP8 && (!a4(ex->s1) || !a4(ex->s3) || !a4(ex->s2))) return MOE_EINVAL;
   if (ex->has_shared) {
     if (!ex->sw1 || !ex->sw3 || !ex->sw2) return MOE_EINVAL;
     if (!aligned16(ex->sw1) || !aligned16(ex->sw3) || !aligned16(ex->sw2)) return MOE_EINVAL;
-    if (ex->wtype == MOE_W_FP8 && (!ex->ss1 || !ex->ss3 || !ex->ss2)) return MOE_EINVAL;
+    if (scaled && (!ex->ss1 || !ex->ss3 || !ex->ss2)) return MOE_EINVAL;
+    if (ex->wtype == MOE_W_MXFP8 && (!a4(ex->ss1) || !a4(ex->ss3) || !a4(ex->ss2))) return MOE_EINVAL;
   }
   return MOE_OK;
 }
@@ -77,8 +84,12 @@ GemmArgs gemm_args(const moe_experts_t* ex, int64_t T, int k, const int32_t* off
   GemmArgs a;
   a.w1 = ex->w1; a.w3 = ex->w3; a.w2 = ex->w2;
   a.sw1 = ex->sw1; a.sw3 = ex->sw3; a.sw2 = ex->sw2;
-  a.s1 = ex->s1; a.s3 = ex->s3; a.s2 = ex->s2;
-  a.ss1 = ex->ss1; a.ss3 = ex->ss3; a.ss2 = ex->ss2;
+  // fp32 128x128 block scales (MOE_W_FP8) or E8M0 bytes (MOE_W_MXFP8); each
+  // kernel family reads them in its own format
+  a.s1 = static_cast<const float*>(ex->s1); a.s3 = static_cast<const float*>(ex->s3);
+  a.s2 = static_cast<const float*>(ex->s2);
+  a.ss1 = static_cast<const float*>(ex->ss1); a.ss3 = static_cast<const float*>(ex->ss3);
+  a.ss2 = static_cast<const float*>(ex->ss2);
   a.E = ex->E; a.H = ex->H; a.I = ex->I; a.has_shared = ex->has_shared; a.k = k;
   a.T = T;
   a.offsets = offsets;
@@ -194,6 +205,22 @@ int moe_quant_rows_fp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, fl
   MOE_GUARD_END
 }
 
+int moe_quant_rows_mxfp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* s, void* stream) {
+  MOE_GUARD_BEGIN
+  if (rows < 0 || cols <= 0) return MOE_EINVAL;
+  if (cols % 32 != 0) return MOE_EUNSUPPORTED;
+  if (rows * (cols / 32) >= kMaxRows) return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !s) return MOE_EINVAL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u)) return MOE_EINVAL;
+  if (overlap(q, (size_t)rows * cols, s, (size_t)rows * (cols / 32)) ||
+      overlap(x, (size_t)rows * cols * 2, q, (size_t)rows * cols) ||
+      overlap(x, (size_t)rows * cols * 2, s, (size_t)rows * (cols / 32)))
+    return MOE_EINVAL;
+  return device_status(launch_quant_rows_mx(x, rows, cols, q, s, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
 int moe_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s,
                          void* stream) {
   MOE_GUARD_BEGIN
@@ -215,8 +242,8 @@ size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k) {
   return kGemmWsBytes;
 }
 
-int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const int32_t* offsets,
-               const int32_t* slot_pair, int64_t T, int k, void* h, float* hs, void* ws, size_t ws_bytes,
+int moe_gemm13(const moe_experts_t* ex, const void* x, const void* xs, const int32_t* offsets,
+               const int32_t* slot_pair, int64_t T, int k, void* h, void* hs, void* ws, size_t ws_bytes,
                void* stream) {
   MOE_GUARD_BEGIN
   int st = check_experts(ex);
@@ -226,26 +253,33 @@ int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const in
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !slot_pair || !h) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(h)) return MOE_EINVAL;
-  const bool fp8 = ex->wtype == MOE_W_FP8;
+  const bool mx = ex->wtype == MOE_W_MXFP8;
+  const bool fp8 = ex->wtype == MOE_W_FP8 || mx;
   if (fp8 && (!xs || !hs)) return MOE_EINVAL;
+  if (mx && (reinterpret_cast<uintptr_t>(xs) & 3u)) return MOE_EINVAL;   // 4-byte scale words
   const int64_t R = T * k + ex->has_shared * T;
   const size_t hbytes = (size_t)R * ex->I * (fp8 ? 1 : 2);
+  const size_t hsbytes = mx ? (size_t)R * (ex->I / 32) : (size_t)R * (ex->I / 128) * 4;
   if (overlap(h, hbytes, x, (size_t)T * ex->H * (fp8 ? 1 : 2))) return MOE_EINVAL;
-  if (fp8 && overlap(hs, (size_t)R * (ex->I / 128) * 4, h, hbytes)) return MOE_EINVAL;
+  if (fp8 && overlap(hs, hsbytes, h, hbytes)) return MOE_EINVAL;
   if (ws == nullptr || ws_bytes < kGemmWsBytes) return MOE_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 3u) return MOE_EINVAL;
   if (overlap(ws, kGemmWsBytes, h, hbytes) || overlap(ws, kGemmWsBytes, x, (size_t)T * ex->H * (fp8 ? 1 : 2)))
     return MOE_EINVAL;
   const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
   hipStream_t s = (hipStream_t)stream;
+  if (mx)
+    return device_status(launch_gemm13_mx(a, static_cast<const uint8_t*>(x), static_cast<const uint8_t*>(xs),
+                                          static_cast<uint8_t*>(h), static_cast<uint8_t*>(hs), static_cast<int*>(ws), s));
   if (fp8)
-    return device_status(launch_gemm13_fp8(a, static_cast<const uint8_t*>(x), xs, static_cast<uint8_t*>(h), hs, s));
+    return device_status(launch_gemm13_fp8(a, static_cast<const uint8_t*>(x), static_cast<const float*>(xs),
+                                           static_cast<uint8_t*>(h), static_cast<float*>(hs), s));
   return device_status(
       launch_gemm13_bf16(a, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(h), static_cast<int*>(ws), s));
   MOE_GUARD_END
 }
 
-int moe_gemm2(const moe_experts_t* ex, const void* h, const float* hs, const int32_t* offsets, int64_t T, int k,
+int moe_gemm2(const moe_experts_t* ex, const void* h, const void* hs, const int32_t* offsets, int64_t T, int k,
               void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
   MOE_GUARD_BEGIN
   (void)ws;
@@ -258,14 +292,21 @@ int moe_gemm2(const moe_experts_t* ex, const void* h, const float* hs, const int
   if (T == 0) return MOE_OK;
   if (!h || !offsets || !y) return MOE_EINVAL;
   if (!aligned16(h) || !aligned16(y)) return MOE_EINVAL;
-  const bool fp8 = ex->wtype == MOE_W_FP8;
+  const bool mx = ex->wtype == MOE_W_MXFP8;
+  const bool fp8 = ex->wtype == MOE_W_FP8 || mx;
   if (fp8 && !hs) return MOE_EINVAL;
+  if (mx && (reinterpret_cast<uintptr_t>(hs) & 3u)) return MOE_EINVAL;   // 4-byte scale words
   const int64_t R = T * k + ex->has_shared * T;
   if (overlap(y, (size_t)R * ex->H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2), h, (size_t)R * ex->I * (fp8 ? 1 : 2)))
     return MOE_EINVAL;
   const GemmArgs a = gemm_args(ex, T, k, offsets, nullptr);
   hipStream_t s = (hipStream_t)stream;
-  if (fp8) return device_status(launch_gemm2_fp8(a, static_cast<const uint8_t*>(h), hs, y, y_dtype, s));
+  if (mx)
+    return device_status(launch_gemm2_mx(a, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(hs), y,
+                                         y_dtype, s));
+  if (fp8)
+    return device_status(
+        launch_gemm2_fp8(a, static_cast<const uint8_t*>(h), static_cast<const float*>(hs), y, y_dtype, s));
   return device_status(launch_gemm2_bf16(a, static_cast<const uint16_t*>(h), y, y_dtype, s));
   MOE_GUARD_END
 }
@@ -298,7 +339,8 @@ struct FwdLayout {
 FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype, bool router) {
   FwdLayout L;
   const int64_t P = T * k, R = P + ex->has_shared * T;
-  const bool fp8 = ex->wtype == MOE_W_FP8;
+  const bool mx = ex->wtype == MOE_W_MXFP8;
+  const bool fp8 = ex->wtype == MOE_W_FP8 || mx;
   size_t off = 0;
   auto take = [&](size_t n) {
     const size_t at = off;
@@ -315,9 +357,9 @@ FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype,
   L.align_ws = take(moe_align_workspace_bytes(T, ex->E, k));
   L.gemm_ws = take(kGemmWsBytes);
   L.xq = take(fp8 ? (size_t)T * ex->H : 0);
-  L.xs = take(fp8 ? (size_t)T * (ex->H / 128) * 4 : 0);
+  L.xs = take(mx ? (size_t)T * (ex->H / 32) : fp8 ? (size_t)T * (ex->H / 128) * 4 : 0);
   L.h = take((size_t)R * ex->I * (fp8 ? 1 : 2));
-  L.hs = take(fp8 ? (size_t)R * (ex->I / 128) * 4 : 0);
+  L.hs = take(mx ? (size_t)R * (ex->I / 32) : fp8 ? (size_t)R * (ex->I / 128) * 4 : 0);
   L.y = take((size_t)R * ex->H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2));
   L.total = off;
   return L;
@@ -356,6 +398,7 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   char* base = static_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
   const int E = ex->E;
+  const bool mx = ex->wtype == MOE_W_MXFP8;
   const bool fp8 = ex->wtype == MOE_W_FP8;
   float* logits = router ? reinterpret_cast<float*>(base + L.logits) : nullptr;
   int32_t* ids = args->topk_ids ? args->topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
@@ -381,7 +424,15 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   e = launch_align(ids, T, E, k, ex->has_shared, counts, offsets, slot_pair, pair_slot, align_ws, s);
   if (e != hipSuccess) return MOE_EDEVICE;
   const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
-  if (fp8) {
+  if (mx) {
+    uint8_t* xsm = reinterpret_cast<uint8_t*>(base + L.xs);
+    uint8_t* hsm = reinterpret_cast<uint8_t*>(base + L.hs);
+    e = launch_quant_rows_mx(args->x, T, ex->H, xq, xsm, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm13_mx(a, xq, xsm, static_cast<uint8_t*>(h), hsm, reinterpret_cast<int*>(base + L.gemm_ws), s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm2_mx(a, static_cast<const uint8_t*>(h), hsm, y, args->y_dtype, s);
+  } else if (fp8) {
     e = launch_quant_rows(args->x, T, ex->H, xq, xs, s);
     if (e != hipSuccess) return MOE_EDEVICE;
     e = launch_gemm13_fp8(a, xq, xs, static_cast<uint8_t*>(h), hs, s);

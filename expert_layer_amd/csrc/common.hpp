@@ -33,6 +33,19 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// MXFP8 (OCP Microscaling): shared exponent of a 32-value block whose largest
+// magnitude is amax: floor(log2(amax)) - 8, clamped to [-127, 127]; -127 for
+// an all-zero block.  Stored as the E8M0 byte X + 127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e;
+  frexpf(amax, &e);   // amax = m * 2^e, 0.5 <= m < 1
+  return min(127, max(-127, e - 9));
+}
+
+// v * 2^n, exact unless the result leaves the normal range (v_ldexp_f32)
+__device__ __forceinline__ float ldexp_f32(float v, int n) { return __builtin_amdgcn_ldexpf(v, n); }
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float wave_max16(float v) {
@@ -59,6 +72,8 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t*
                              hipStream_t s);
 hipError_t launch_quant_blocks(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q,
                                float* sc, hipStream_t s);
+hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
+                                hipStream_t s);
 
 hipError_t launch_router_split(const float* w, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s);
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* hi, const uint16_t* lo, float* logits,
@@ -86,6 +101,14 @@ bool tiled_gemm13_ok(const GemmArgs& a);
 bool tiled_gemm2_ok(const GemmArgs& a);
 hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s);
 hipError_t launch_gemm2_tiled(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s);
+
+// MXFP8 (E8M0 bytes per 32 K): xs [T, H/32], hs [R, I/32]; weight scales in
+// GemmArgs s1/s3/s2 (and the shared ones) point to bytes [rows, K/32]
+bool tiled_mx_gemm2_ok(const GemmArgs& a);
+hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
+                            int* sync, hipStream_t s);
+hipError_t launch_gemm2_mx(const GemmArgs& a, const uint8_t* hq, const uint8_t* hs, void* y, int y_dtype,
+                           hipStream_t s);
 
 bool tiled_fp8_gemm13_ok(const GemmArgs& a);
 bool tiled_fp8_gemm2_ok(const GemmArgs& a);

@@ -5,6 +5,10 @@
 //            checkpoint format of the PR #54160 report, implementation item 4).
 // Scale = amax / 448 with a correctly rounded fp32 division (1 when amax is 0);
 // code = e4m3(fp32(v / scale)).
+//  * rows_mx: MXFP8 (OCP Microscaling, the format the PR #54160 report lists
+//            beside the 128x128 scales): per row, per 32 columns, an E8M0
+//            byte X + 127 with X = floor(log2(amax)) - 8 and codes
+//            e4m3(v * 2^-X) (exact power-of-two scaling, then RNE/saturation).
 #include "common.hpp"
 
 namespace moe355 {
@@ -90,7 +94,49 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
   if (threadIdx.x == 0) sc[blk] = s;
 }
 
+// 4 lanes per 32-column MX block, 8 columns (16 bytes of bf16) per lane.
+__global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int cols, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ sc) {
+  const int nb = cols / 32;
+  const int64_t blk = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int sub = threadIdx.x & 3;
+  const bool live = blk < rows * nb;
+  const int64_t r = live ? blk / nb : 0;
+  const int c0 = live ? (int)(blk % nb) * 32 + sub * 8 : 0;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) raw = *reinterpret_cast<const uint4*>(x + r * cols + c0);
+  float v[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int X = mx_exponent(amax);
+  uint32_t lo = f32x2_to_e4m3(ldexp_f32(v[0], -X), ldexp_f32(v[1], -X)) |
+                (f32x2_to_e4m3(ldexp_f32(v[2], -X), ldexp_f32(v[3], -X)) << 16);
+  uint32_t hi = f32x2_to_e4m3(ldexp_f32(v[4], -X), ldexp_f32(v[5], -X)) |
+                (f32x2_to_e4m3(ldexp_f32(v[6], -X), ldexp_f32(v[7], -X)) << 16);
+  if (live) {
+    *reinterpret_cast<uint2*>(q + r * cols + c0) = make_uint2(lo, hi);
+    if (sub == 0) sc[blk] = (uint8_t)(X + 127);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
+                                hipStream_t s) {
+  const int64_t blocks = rows * (cols / 32);
+  quant_rows_mx_kernel<<<(unsigned)((blocks + 63) / 64), 256, 0, s>>>(x, rows, cols, q, sc);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
                              hipStream_t s) {

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE355_ABI_VERSION 1
+#define MOE355_ABI_VERSION 2
 
 enum {
   MOE_OK = 0,
@@ -56,7 +56,7 @@ enum {
 };
 
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };  /* y_dtype */
-enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1 };          /* moe_experts_t.wtype */
+enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_MXFP8 = 2 };   /* moe_experts_t.wtype */
 
 int moe_abi_version(void);
 const char* moe_status_string(int status);
@@ -124,22 +124,40 @@ int moe_quant_rows_fp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, fl
 int moe_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, uint8_t* q, float* s,
                          void* stream);
 
+/* ------------------------------------------------------------------ MXFP8 helper
+ * MXFP8, the microscaling FP8 format the PR #54160 report lists beside the
+ * 128x128 blockwise scales (implementation item 4), as the OCP Microscaling
+ * definition gives it: per row, every 32 consecutive columns share an E8M0
+ * scale byte X + 127 with X = floor(log2(amax)) - 8 clamped to [-127, 127]
+ * (-127 for an all-zero block); codes are E4M3FN(v * 2^-X), round to nearest
+ * even, saturating at +-448.
+ * moe_quant_rows_mxfp8: x bf16 [rows,cols] -> q [rows,cols], s uint8
+ *   [rows, cols/32].  Used for activations (K along the columns) and, offline,
+ *   for weights stored with K along the rows' columns (w1, w3 as [E*I, H], w2
+ *   as [E*H, I]).  cols must be a multiple of 32; x 16-byte and q 8-byte
+ *   aligned; x, q and s must not overlap.
+ */
+int moe_quant_rows_mxfp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* s, void* stream);
+
 /* ------------------------------------------------------------------ experts
  * SwiGLU experts: h = SiLU(x.w1^T) * (x.w3^T) (w1 = gate, w3 = up),
  * y = h.w2^T.  Routed: w1, w3 [E,I,H], w2 [E,H,I].  Shared expert (if
  * has_shared): sw1, sw3 [I,H], sw2 [H,I].  wtype MOE_W_BF16: bf16 weights,
  * scale pointers ignored.  wtype MOE_W_FP8: e4m3 codes plus fp32 128x128 block
  * scales s1, s3 [E,I/128,H/128], s2 [E,H/128,I/128], ss1, ss3 [I/128,H/128],
- * ss2 [H/128,I/128].  The struct itself is host memory; the pointers in it are
- * device pointers.
+ * ss2 [H/128,I/128].  wtype MOE_W_MXFP8: e4m3 codes plus uint8 E8M0 scales per
+ * weight row per 32 K (moe_quant_rows_mxfp8): s1, s3 [E,I,H/32], s2
+ * [E,H,I/32], ss1, ss3 [I,H/32], ss2 [H,I/32], 4-byte aligned (MOE_EINVAL
+ * otherwise); H must be a multiple of 256 (MOE_EUNSUPPORTED otherwise).  The struct itself is host memory; the
+ * pointers in it are device pointers.
  */
 typedef struct moe_experts_t {
   int wtype;
   int E, H, I, has_shared;
   const void *w1, *w3, *w2;
-  const float *s1, *s3, *s2;
+  const void *s1, *s3, *s2;     /* fp32 (MOE_W_FP8) or uint8 E8M0 (MOE_W_MXFP8) */
   const void *sw1, *sw3, *sw2;
-  const float *ss1, *ss3, *ss2;
+  const void *ss1, *ss3, *ss2;
 } moe_experts_t;
 
 /* ------------------------------------------------------------------ stages 2-3: Gate-Up GEMM
@@ -154,10 +172,14 @@ typedef struct moe_experts_t {
  *   sums over each 128-wide K block are scaled by xs[t,kb] * s[g,n/128,kb];
  *   h is requantised per row per 128 columns into h e4m3 [R,I] and hs fp32
  *   [R,I/128] with the same rule as moe_quant_rows_fp8.
+ * mxfp8: x e4m3 [T,H] with xs uint8 [T,H/32] (moe_quant_rows_mxfp8, 4-byte
+ *   aligned); the matrix cores apply the E8M0 scales of both operands per 32 K;
+ *   h is requantised per row per 32 columns with the same rule as
+ *   moe_quant_rows_mxfp8 into h e4m3 [R,I] and hs uint8 [R,I/32].
  * offsets, slot_pair: from moe_align.
  * ws: device scratch of moe_gemm_workspace_bytes bytes, 4-byte aligned; its
  *   contents need not be initialised (the call clears what it uses, on its
- *   stream).  The bf16 kernel for large groups keeps one counter per XCD in
+ *   stream).  The bf16 kernel for large groups and the MXFP8 kernel keep one counter per XCD in
  *   it, at which the workgroups of that XCD meet after every round of tiles
  *   so that tiles sharing operands stream them through L2 together.  The
  *   waits are bounded, so the workspace affects timing only, never results;
@@ -166,17 +188,18 @@ typedef struct moe_experts_t {
  *   or misaligned: MOE_EINVAL.
  */
 size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k);
-int moe_gemm13(const moe_experts_t* ex, const void* x, const float* xs, const int32_t* offsets,
-               const int32_t* slot_pair, int64_t T, int k, void* h, float* hs, void* ws,
+int moe_gemm13(const moe_experts_t* ex, const void* x, const void* xs, const int32_t* offsets,
+               const int32_t* slot_pair, int64_t T, int k, void* h, void* hs, void* ws,
                size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ stage 4: Down GEMM
  * y[s] = h[s].w2[g]^T for every slot s of group g (fp32 accumulation; fp8
- * partial sums per 128-wide K block scaled by hs[s,kb] * s2[g,n/128,kb]).
+ * partial sums per 128-wide K block scaled by hs[s,kb] * s2[g,n/128,kb];
+ * mxfp8: hs uint8 [R,I/32], 4-byte aligned, scales applied per 32 K).
  * y is fp32 (y_dtype MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16), [R,H].
  * ws, ws_bytes: reserved, unused (NULL and 0 are accepted).
  */
-int moe_gemm2(const moe_experts_t* ex, const void* h, const float* hs, const int32_t* offsets,
+int moe_gemm2(const moe_experts_t* ex, const void* h, const void* hs, const int32_t* offsets,
               int64_t T, int k, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ stage 5: combine

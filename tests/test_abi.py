@@ -34,14 +34,14 @@ def L():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert sorted(moe.exported_symbols()) == names
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert moe.moe_status_string(0) == "ok"
     for s in range(1, 5):
         assert moe.moe_status_string(s) not in ("ok", "unknown status")
@@ -85,6 +85,17 @@ def test_quant_validation(L):
     assert L.moe_quant_blocks_fp8(A, -1, 128, 128, B, C, None) == moe.MOE_EINVAL
 
 
+def test_quant_mxfp8_validation(L):
+    qm = L.moe_quant_rows_mxfp8
+    assert qm(A, 4, 48, B, C, None) == moe.MOE_EUNSUPPORTED          # cols % 32
+    assert qm(A, -1, 64, B, C, None) == moe.MOE_EINVAL
+    assert qm(A + 2, 4, 64, B, C, None) == moe.MOE_EINVAL             # x misaligned
+    assert qm(A, 4, 64, B + 4, C, None) == moe.MOE_EINVAL             # q misaligned
+    assert qm(A, 4, 64, B, B + 8, None) == moe.MOE_EINVAL             # s overlaps q
+    assert qm(A, 4, 64, None, C, None) == moe.MOE_EINVAL
+    assert qm(A, 0, 64, B, C, None) == moe.MOE_OK
+
+
 def _experts(**kw):
     d = dict(wtype=0, E=8, H=256, I=128, has_shared=0, w1=A, w3=B, w2=C)
     d.update(kw)
@@ -108,6 +119,14 @@ def test_gemm_validation(L):
     assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, x, None, None, 0, None) == moe.MOE_EINVAL       # h aliases x
     assert g13(ctypes.byref(ok), x, None, off, sp, 0, 2, h, None, None, 0, None) == moe.MOE_OK
     assert g13(None, x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL
+    mx = _experts(wtype=2, s1=A, s3=B, s2=C)
+    assert g13(ctypes.byref(mx), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EINVAL   # no xs/hs
+    assert g13(ctypes.byref(_experts(wtype=2)), x, D, off, sp, 4, 2, h, D + 4096, None, 0, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(_experts(wtype=2, s1=A, s3=B, s2=C, H=384)), x, D, off, sp, 4, 2, h, D + 4096,
+               None, 0, None) == moe.MOE_EUNSUPPORTED                                           # MX needs H % 256
+    assert g13(ctypes.byref(mx), x, D + 2, off, sp, 4, 2, h, D + 4096, D + 8192, 256, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(_experts(wtype=2, s1=A + 2, s3=B, s2=C)), x, D, off, sp, 4, 2, h, D + 4096,
+               D + 8192, 256, None) == moe.MOE_EINVAL                                           # scales misaligned
     need = L.moe_gemm_workspace_bytes(ctypes.byref(ok), 4, 2)
     assert need > 0
     assert g13(ctypes.byref(ok), x, None, off, sp, 4, 2, h, None, None, 0, None) == moe.MOE_EWORKSPACE

@@ -68,6 +68,51 @@ def test_small_fp8(wl):
     check_layer(wl, _inputs(wl), y_dtype=torch.float32)
 
 
+MX_SMALL = [
+    W("mx-medium", T=300, H=512, E=16, k=4, I=256, shared=1, wtype="mxfp8", seed=24),
+    W("mx-ragged", T=37, H=256, E=8, k=3, I=384, shared=0, wtype="mxfp8", seed=25),
+    W("mx-zipf", T=400, H=256, E=32, k=8, I=256, shared=1, wtype="mxfp8", bias="all", seed=26),
+    W("mx-tiny-groups", T=16, H=512, E=64, k=8, I=256, shared=1, wtype="mxfp8", seed=27),
+]
+
+
+@pytest.mark.parametrize("wl", MX_SMALL, ids=[w.name for w in MX_SMALL])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16], ids=["yf32", "ybf16"])
+def test_small_mxfp8(wl, ydt):
+    check_layer(wl, _inputs(wl), y_dtype=ydt)
+
+
+def test_mxfp8_quantiser_exhaustive_over_bf16():
+    """Every finite bf16 value through the GPU MXFP8 quantiser, as given and
+    scaled to hit saturation, ties and the clamped exponent range: codes and
+    scale bytes equal the oracle's bit for bit."""
+    import expert_layer_amd as moe
+    from oracle import oracle as orc
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    expo = (allbits >> 7) & 0xFF
+    finite = allbits[expo != 0xFF]
+    n = finite.size - finite.size % 256
+    rng = np.random.default_rng(9)
+    rows = rng.permutation(finite[:n]).reshape(-1, 256)
+    # plus a row of bf16 subnormals (clamped exponent) and an all-zero row
+    rows = np.concatenate([rows, np.arange(1, 257, dtype=np.uint16)[None], np.zeros((1, 256), np.uint16)])
+    vals = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).float().numpy()
+    with np.errstate(over="ignore"):
+        scaled = vals * np.ldexp(1.0, rng.integers(-40, 40, size=(vals.shape[0], 1))).astype(np.float32)
+    scaled = np.where(np.abs(scaled) < 3.0e38, scaled, 0.0).astype(np.float32)   # finite inputs only
+    scaled_bits = torch.from_numpy(scaled).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for data in (rows, scaled_bits):
+        xg = torch.from_numpy(data.view(np.int16)).view(torch.bfloat16).cuda()
+        q = torch.empty(data.shape, dtype=torch.uint8, device="cuda")
+        s = torch.empty((data.shape[0], data.shape[1] // 32), dtype=torch.uint8, device="cuda")
+        moe.moe_quant_rows_mxfp8(xg, q, s)
+        torch.cuda.synchronize()
+        rq, rs = orc.quant_rows_mx(data)
+        assert np.array_equal(s.cpu().numpy(), rs), "scale bytes differ"
+        bad = np.sum(q.cpu().numpy() != rq)
+        assert bad == 0, f"{bad} codes differ"
+
+
 def test_forced_ties_and_one_hot():
     """Integer logits (many exact ties) and a batch where every token picks expert 5 first."""
     wl = W("ties", T=128, H=256, E=16, k=4, I=128, shared=1, seed=30)
@@ -168,7 +213,7 @@ def test_fp8_codec_exhaustive_over_bf16():
 # ---------------------------------------------------------------- the five layer configurations
 @pytest.mark.parametrize("name,ydt", [("tiny", torch.float32), ("decode", torch.float32),
                                       ("prefill", torch.bfloat16), ("fp8", torch.float32),
-                                      ("router", torch.bfloat16)])
+                                      ("mxfp8", torch.float32), ("router", torch.bfloat16)])
 def test_layer_configs(name, ydt):
     wl = workloads.WORKLOADS[name]
     d = _inputs(wl)
