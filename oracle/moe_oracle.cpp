@@ -564,6 +564,40 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
   });
 }
 
+// ---------------------------------------------------------------- combine / norm
+// Stage 5 on given expert outputs y [R,H] (fp32 values): out[t] =
+// sum_j w[t,j] * y[pair_slot[t*k+j]] + shared * y[T*k + t], in double.
+void orc_combine(const float* y, const int32_t* pair_slot, const float* w, int64_t T, int k, int H,
+                 int has_shared, double* out) {
+  const int64_t P = T * k;
+  for (int64_t t = 0; t < T; ++t)
+    for (int m = 0; m < H; ++m) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += static_cast<double>(w[t * k + j]) * y[(int64_t)pair_slot[t * k + j] * H + m];
+      if (has_shared) acc += y[(P + t) * H + m];
+      out[t * H + m] = acc;
+    }
+}
+
+// Residual add + RMSNorm, the single-GPU half of the HPC-Ops page's fused
+// AllReduce+Norm (technical principles: RMSNorm(AllReduce(x) + residual,
+// weight); on one GPU the all-reduce is the identity):
+//   s = x + residual,  out = s / sqrt(mean(s^2) + eps) * weight   (per row, in double)
+// x [rows,H] double, residual and weight bf16; s and out [rows,H] double.
+void orc_add_rmsnorm(const double* x, const uint16_t* residual, const uint16_t* weight, double eps,
+                     int64_t rows, int H, double* s, double* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    double ssq = 0.0;
+    for (int m = 0; m < H; ++m) {
+      const double v = x[r * H + m] + bf16_value(residual[r * H + m]);
+      s[r * H + m] = v;
+      ssq += v * v;
+    }
+    const double inv = 1.0 / std::sqrt(ssq / H + eps);
+    for (int m = 0; m < H; ++m) out[r * H + m] = s[r * H + m] * inv * bf16_value(weight[m]);
+  }
+}
+
 int orc_version(void) { return 1; }
 
 }  // extern "C"

@@ -73,6 +73,8 @@ def lib():
         L.orc_expert_bf16.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_expert_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_layer_rows.argtypes = [ctypes.POINTER(_Layer), _P, _P, _P, _P, _I32, _P, _I64, _P, _I32]
+        L.orc_combine.argtypes = [_P, _P, _P, _I64, _I32, _I32, _I32, _P]
+        L.orc_add_rmsnorm.argtypes = [_P, _P, _P, ctypes.c_double, _I64, _I32, _P, _P]
         _lib = L
     return _lib
 
@@ -262,3 +264,27 @@ def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None):
     lib().orc_layer_rows(ctypes.byref(layer.c), _ptr(x), _ptr(xs), _ptr(ids), _ptr(weights), k,
                          _ptr(rows), rows.size, _ptr(out), nthreads or default_threads())
     return out
+
+
+# ------------------------------------------------------------------ combine / norm
+def combine(y, pair_slot, w, T, k, has_shared):
+    """Stage 5 on given expert outputs y [R,H] (fp32 values): double [T,H]."""
+    y = _c(y, np.float32)
+    pair_slot = _c(pair_slot, np.int32)
+    w = _c(w, np.float32)
+    H = y.shape[1]
+    out = np.empty((T, H), np.float64)
+    lib().orc_combine(_ptr(y), _ptr(pair_slot), _ptr(w), T, k, H, int(has_shared), _ptr(out))
+    return out
+
+
+def add_rmsnorm(x, residual_bits, weight_bits, eps):
+    """s = x + residual, out = s / sqrt(mean(s^2) + eps) * weight, per row (double)."""
+    x = _c(x, np.float64)
+    residual_bits = _c(residual_bits, np.uint16)
+    weight_bits = _c(weight_bits, np.uint16)
+    rows, H = x.shape
+    s = np.empty((rows, H), np.float64)
+    out = np.empty((rows, H), np.float64)
+    lib().orc_add_rmsnorm(_ptr(x), _ptr(residual_bits), _ptr(weight_bits), float(eps), rows, H, _ptr(s), _ptr(out))
+    return s, out
