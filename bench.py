@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--residual-norm", action="store_true",
+                    help="fuse a residual add + RMSNorm into the combine stage (bf16 residual and weight)")
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
                     help="time the chain as eager launches (default) or as one captured HIP graph per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
@@ -192,6 +194,10 @@ def main():
         hi, lo = split_router(d["router_w"])
     kw = dict(logits=None if wl.router else d["logits"], router_hi=hi, router_lo=lo, bias=d["bias"],
               bias_rows=d["bias_rows"])
+    if args.residual_norm:
+        g = torch.Generator(device=dev).manual_seed(wl.seed + 17)
+        kw["residual"] = torch.randn((wl.T, wl.H), generator=g, device=dev).to(torch.bfloat16)
+        kw["norm_weight"] = (1.0 + 0.1 * torch.randn(wl.H, generator=g, device=dev)).to(torch.bfloat16)
     if fp8:   # fp8 weights are quantised once; the bf16 copies are not needed any more
         for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2"):
             d[n] = None
@@ -285,7 +291,7 @@ def main():
            "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
                       "shared": wl.shared, "weights": wl.wtype, "router": wl.router,
                       "y_dtype": "f32" if y_dtype == torch.float32 else "bf16", "seed": wl.seed,
-                      "launch": args.launch},
+                      "launch": args.launch, "residual_norm": bool(args.residual_norm)},
            "roofline": roof, "layer": layer_info, "cpu_baseline": cpu,
            "kernel_source_hash": src_hash}
     print(json.dumps(rec), flush=True)

@@ -61,6 +61,7 @@ _SIGS = {
     "moe_gemm13": (_I32, [ctypes.POINTER(moe_experts_t), _P, _P, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "moe_gemm2": (_I32, [ctypes.POINTER(moe_experts_t), _P, _P, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]),
     "moe_combine": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _P]),
+    "moe_combine_rmsnorm": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _P, ctypes.c_float, _P, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [ctypes.POINTER(moe_experts_t), _I64, _I32, _I32]),
     "moe_forward": (_I32, [ctypes.POINTER(moe_experts_t), ctypes.POINTER(moe_forward_args_t), _P, _SZ, _P]),
 }
@@ -246,6 +247,19 @@ def moe_combine(y, pair_slot, topk_w, T, k, has_shared, out):
     H = out.shape[1]
     _check(lib().moe_combine(_ptr(y), y_dtype, _ptr(pair_slot), _ptr(topk_w), T, k, H, int(has_shared), _ptr(out),
                              _stream(y)), "moe_combine")
+
+
+def moe_combine_rmsnorm(y, pair_slot, topk_w, T, k, has_shared, residual, weight, eps, out, res_out=None):
+    """Combine + residual add + RMSNorm: out = RMSNorm(combine + residual, weight); res_out = the sum."""
+    _expect(residual, torch.bfloat16, "residual")
+    _expect(weight, torch.bfloat16, "weight")
+    _expect(out, torch.bfloat16, "out")
+    _expect(res_out, torch.bfloat16, "res_out")
+    y_dtype = MOE_DTYPE_F32 if y.dtype == torch.float32 else MOE_DTYPE_BF16
+    H = out.shape[1]
+    _check(lib().moe_combine_rmsnorm(_ptr(y), y_dtype, _ptr(pair_slot), _ptr(topk_w), T, k, H, int(has_shared),
+                                     _ptr(residual), _ptr(weight), float(eps), _ptr(out), _ptr(res_out), _stream(y)),
+           "moe_combine_rmsnorm")
 
 
 # ------------------------------------------------------------------ whole chain

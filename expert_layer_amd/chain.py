@@ -13,7 +13,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (Experts, moe_align, moe_align_workspace_bytes, moe_combine, moe_gemm2, moe_gemm13,
+from . import (Experts, moe_align, moe_align_workspace_bytes, moe_combine, moe_combine_rmsnorm, moe_gemm2,
+               moe_gemm13,
                moe_gemm_workspace_bytes,
                moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_quant_rows_mxfp8, moe_route, moe_router_gemm,
                moe_router_split)
@@ -115,9 +116,12 @@ def split_router(router_w):
 
 
 def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, router_lo=None, bias=None,
-              bias_rows=None, stages=None):
+              bias_rows=None, stages=None, residual=None, norm_weight=None, eps=1e-6):
     """Enqueue the chain on torch's current stream.  ``stages`` (optional) maps a
-    stage name to a (start_event, end_event) pair recorded around that stage."""
+    stage name to a (start_event, end_event) pair recorded around that stage.
+    With ``residual`` (bf16 [T,H]) and ``norm_weight`` (bf16 [H]) the combine
+    also adds the residual and applies RMSNorm: ``b.out`` receives the
+    normalised rows and ``residual`` is updated in place to the sum."""
     def ev(name, i):
         if stages is not None and name in stages:
             stages[name][i].record()
@@ -153,6 +157,10 @@ def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, route
     moe_gemm2(ex, b.h, b.hs, b.offsets, T, k, b.y)
     ev("gemm2", 1)
     ev("combine", 0)
-    moe_combine(b.y, b.pair_slot, b.w, T, k, layer.shared, b.out)
+    if residual is None:
+        moe_combine(b.y, b.pair_slot, b.w, T, k, layer.shared, b.out)
+    else:
+        moe_combine_rmsnorm(b.y, b.pair_slot, b.w, T, k, layer.shared, residual, norm_weight, eps, b.out,
+                            res_out=residual)
     ev("combine", 1)
     return b

@@ -329,6 +329,35 @@ int moe_combine(const void* y, int y_dtype, const int32_t* pair_slot, const floa
   MOE_GUARD_END
 }
 
+int moe_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, const float* topk_w, int64_t T,
+                        int k, int H, int has_shared, const uint16_t* residual, const uint16_t* weight, float eps,
+                        uint16_t* out, uint16_t* res_out, void* stream) {
+  MOE_GUARD_BEGIN
+  if (T < 0 || k <= 0 || H <= 0) return MOE_EINVAL;
+  if (has_shared != 0 && has_shared != 1) return MOE_EINVAL;
+  if (!(eps >= 0.0f) || !(eps < 3.0e38f)) return MOE_EINVAL;   // finite, >= 0 (NaN fails)
+  if (k > 32 || H % 128 != 0 || H > 32768) return MOE_EUNSUPPORTED;
+  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16) return MOE_EUNSUPPORTED;
+  if (T * k + has_shared * T >= kMaxRows) return MOE_EUNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y || !pair_slot || !topk_w || !residual || !weight || !out) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(residual) || !aligned16(weight)) return MOE_EINVAL;
+  if (res_out && !aligned16(res_out)) return MOE_EINVAL;
+  const int64_t R = T * k + has_shared * T;
+  const size_t rowb = (size_t)T * H * 2;
+  const size_t yb = (size_t)R * H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2);
+  if (overlap(out, rowb, y, yb) || overlap(out, rowb, residual, rowb) || overlap(out, rowb, weight, (size_t)H * 2))
+    return MOE_EINVAL;
+  if (res_out) {
+    if (overlap(res_out, rowb, out, rowb) || overlap(res_out, rowb, y, yb) || overlap(res_out, rowb, weight, (size_t)H * 2))
+      return MOE_EINVAL;
+    if (res_out != residual && overlap(res_out, rowb, residual, rowb)) return MOE_EINVAL;   // in place or disjoint
+  }
+  return device_status(launch_combine_rmsnorm(y, y_dtype, pair_slot, topk_w, T, k, H, has_shared, residual, weight,
+                                              eps, out, res_out, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
 // ------------------------------------------------------------------ whole chain
 namespace {
 

@@ -2,6 +2,14 @@
 //   out[t] = sum_j w[t,j] * y[pair_slot[t*k+j]] + shared * y[P+t]
 // in a fixed order (j ascending, then the shared expert) in fp32, one
 // round-to-nearest-even to bf16.  No atomics: one workgroup owns a token.
+//
+// combine_rmsnorm_kernel adds the residual stream and applies RMSNorm in the
+// same pass, the single-GPU half of the fused AllReduce+Norm of the HPC-Ops
+// page (technical principles: RMSNorm(AllReduce(x) + residual, weight)):
+//   s = combine(t) + residual[t]   (fp32, the combine sum unrounded)
+//   res_out[t] = bf16(s)           (optional; may be residual itself)
+//   out[t] = bf16(s * 1/sqrt(mean(s^2) + eps) * weight)
+// The row of s stays in LDS between the reduction and the scaling.
 #include "common.hpp"
 
 namespace moe355 {
@@ -66,7 +74,122 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
   }
 }
 
+// y terms of one token for 8 columns starting at c, summed in fixed order
+template <int YBF16>
+__device__ __forceinline__ void combine8(const void* __restrict__ yv, const int32_t* slot, const float* wt,
+                                         int nterm, int k, int64_t P, int64_t t, int H, int c, float acc[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < nterm; ++j) {
+    const bool sh = j == k;
+    const int64_t s = sh ? P + t : (int64_t)slot[j];
+    const float a = sh ? 1.0f : wt[j];
+    float v[8];
+    if (YBF16) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yv) + s * H + c);
+      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(u[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(yv) + s * H + c);
+      const float4 a0 = p[0], a1 = p[1];
+      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    }
+    if (sh) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(a, v[i], acc[i]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float v[8]) {
+  uint4 o;
+  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+  o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+  return o;
+}
+
+template <int YBF16>
+__global__ __launch_bounds__(kThreads) void combine_rmsnorm_kernel(
+    const void* __restrict__ yv, const int32_t* __restrict__ pair_slot, const float* __restrict__ w, int64_t T,
+    int k, int H, int has_shared, const uint16_t* residual, const uint16_t* __restrict__ weight, float eps,
+    uint16_t* __restrict__ out, uint16_t* res_out) {
+  extern __shared__ float srow[];   // H floats: the row of s
+  __shared__ int32_t slot[33];
+  __shared__ float wt[33];
+  __shared__ float part[kThreads / 64];
+  const int64_t t = blockIdx.x;
+  const int64_t P = T * k;
+  if (threadIdx.x < k) {
+    slot[threadIdx.x] = pair_slot[t * k + threadIdx.x];
+    wt[threadIdx.x] = w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int nterm = k + (has_shared ? 1 : 0);
+  float ssq = 0.0f;
+  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+    float acc[8];
+    combine8<YBF16>(yv, slot, wt, nterm, k, P, t, H, c, acc);
+    // residual read before res_out is written (same thread, same columns), so
+    // res_out may be residual itself
+    const uint4 raw = *reinterpret_cast<const uint4*>(residual + t * H + c);
+    const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_to_f32(u[i] & 0xFFFFu);
+      acc[2 * i + 1] += bf16_to_f32(u[i] >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      srow[c + i] = acc[i];
+      ssq = __builtin_fmaf(acc[i], acc[i], ssq);
+    }
+    if (res_out) *reinterpret_cast<uint4*>(res_out + t * H + c) = pack_bf16x8(acc);
+  }
+  // fixed-order reduction: within each wave, then over the waves
+  for (int off = 32; off >= 1; off >>= 1) ssq += __shfl_xor(ssq, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ssq;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) tot += part[i];
+  const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(tot, (float)H) + eps));
+  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(weight + c);
+    const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = srow[c + 2 * i] * inv * bf16_to_f32(u[i] & 0xFFFFu);
+      o[2 * i + 1] = srow[c + 2 * i + 1] * inv * bf16_to_f32(u[i] >> 16);
+    }
+    *reinterpret_cast<uint4*>(out + t * H + c) = pack_bf16x8(o);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
+                                  int k, int H, int has_shared, const uint16_t* residual, const uint16_t* weight,
+                                  float eps, uint16_t* out, uint16_t* res_out, hipStream_t s) {
+  const size_t lds = (size_t)H * sizeof(float);
+  if (y_dtype == 1)
+    combine_rmsnorm_kernel<1><<<(unsigned)T, kThreads, lds, s>>>(y, pair_slot, w, T, k, H, has_shared, residual,
+                                                                 weight, eps, out, res_out);
+  else
+    combine_rmsnorm_kernel<0><<<(unsigned)T, kThreads, lds, s>>>(y, pair_slot, w, T, k, H, has_shared, residual,
+                                                                 weight, eps, out, res_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
                           int k, int H, int has_shared, uint16_t* out, hipStream_t s) {

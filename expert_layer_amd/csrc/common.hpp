@@ -75,6 +75,10 @@ hipError_t launch_quant_blocks(const uint16_t* w, int64_t mats, int rows, int co
 hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                                 hipStream_t s);
 
+hipError_t launch_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
+                                  int k, int H, int has_shared, const uint16_t* residual, const uint16_t* weight,
+                                  float eps, uint16_t* out, uint16_t* res_out, hipStream_t s);
+
 hipError_t launch_router_split(const float* w, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s);
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* hi, const uint16_t* lo, float* logits,
                               int64_t T, int H, int E, hipStream_t s);

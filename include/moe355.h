@@ -211,6 +211,22 @@ int moe_gemm2(const moe_experts_t* ex, const void* h, const void* hs, const int3
 int moe_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* topk_w, int64_t T,
                 int k, int H, int has_shared, uint16_t* out, void* stream);
 
+/* ------------------------------------------------------------------ combine + residual + RMSNorm
+ * The combine above fused with a residual add and RMSNorm: the single-GPU half
+ * of the HPC-Ops page's fused AllReduce+Norm (technical principles:
+ * RMSNorm(AllReduce(x) + residual, weight); the all-reduce is the identity on
+ * one GPU).  Per token t:
+ *   s = combine(t) + residual[t]      (fp32; the combine sum is not rounded first)
+ *   res_out[t] = bf16(s)              (optional, NULL to skip; may be residual itself)
+ *   out[t] = bf16(s / sqrt(mean_H(s^2) + eps) * weight)
+ * residual, out, res_out bf16 [T,H]; weight bf16 [H]; eps finite and >= 0.
+ * H must be a multiple of 128 and at most 32768.  All arrays 16-byte aligned;
+ * out overlaps nothing; res_out overlaps nothing except being exactly residual.
+ */
+int moe_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, const float* topk_w, int64_t T,
+                        int k, int H, int has_shared, const uint16_t* residual, const uint16_t* weight, float eps,
+                        uint16_t* out, uint16_t* res_out, void* stream);
+
 /* ------------------------------------------------------------------ the whole chain
  * Convenience entry point that enqueues the chain on one stream:
  * [router_gemm] -> route -> align -> [quant_rows_fp8] -> gemm13 -> gemm2 -> combine.

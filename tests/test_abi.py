@@ -34,7 +34,7 @@ def L():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert sorted(moe.exported_symbols()) == names
@@ -146,6 +146,24 @@ def test_combine_validation(L):
     assert cb(A, 0, B, C, 4, 2, 256, 3, D, None) == moe.MOE_EINVAL
     assert cb(A, 0, B, C, 4, 2, 256, 0, A + 16, None) == moe.MOE_EINVAL    # out overlaps y
     assert cb(A, 0, B, C, 0, 2, 256, 0, D, None) == moe.MOE_OK
+
+
+def test_combine_rmsnorm_validation(L):
+    cr = L.moe_combine_rmsnorm
+    F = ctypes.c_float
+    E_ = 0x2100000   # another fake buffer
+    args = lambda **kw: {**dict(y=A, yd=0, ps=B, w=C, T=4, k=2, H=256, sh=0, res=D, wt=E_, eps=F(1e-6),
+                                out=0x2900000, ro=None), **kw}
+    call = lambda a: cr(a["y"], a["yd"], a["ps"], a["w"], a["T"], a["k"], a["H"], a["sh"], a["res"], a["wt"],
+                        a["eps"], a["out"], a["ro"], None)
+    assert call(args(eps=F(-1.0))) == moe.MOE_EINVAL
+    assert call(args(eps=F(float("nan")))) == moe.MOE_EINVAL
+    assert call(args(H=200)) == moe.MOE_EUNSUPPORTED
+    assert call(args(H=65536)) == moe.MOE_EUNSUPPORTED
+    assert call(args(res=None)) == moe.MOE_EINVAL
+    assert call(args(out=D + 64)) == moe.MOE_EINVAL                # out overlaps residual
+    assert call(args(ro=D + 64)) == moe.MOE_EINVAL                 # partial overlap with residual
+    assert call(args(T=0)) == moe.MOE_OK
 
 
 def test_forward_validation(L):

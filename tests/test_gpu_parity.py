@@ -251,3 +251,35 @@ def test_graph_replay_matches_eager(shape):
         run_chain(layer, b, d["x"], wl.k, **kw)     # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(b.out, want), f"eager after replay {i}"
+
+
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16], ids=["yf32", "ybf16"])
+def test_combine_rmsnorm_stage(ydt):
+    """combine + residual + RMSNorm on the GPU's own y against the oracle's
+    combine and add+RMSNorm in double; in place equals out of place bit for bit."""
+    import expert_layer_amd as moe
+    from oracle import oracle as orc
+    wl = W("norm", T=300, H=512, E=16, k=4, I=256, shared=1, seed=51)
+    d = _inputs(wl)
+    _, b, _ = run_gpu(wl, d, y_dtype=ydt)
+    g = torch.Generator(device="cuda").manual_seed(52)
+    residual = torch.randn((wl.T, wl.H), generator=g, device="cuda").to(torch.bfloat16)
+    weight = (1.0 + 0.1 * torch.randn(wl.H, generator=g, device="cuda")).to(torch.bfloat16)
+    eps = 1e-6
+    out = torch.empty_like(residual)
+    res_out = torch.empty_like(residual)
+    moe.moe_combine_rmsnorm(b.y, b.pair_slot, b.w, wl.T, wl.k, wl.shared, residual, weight, eps, out, res_out)
+    res_in_place = residual.clone()
+    out2 = torch.empty_like(residual)
+    moe.moe_combine_rmsnorm(b.y, b.pair_slot, b.w, wl.T, wl.k, wl.shared, res_in_place, weight, eps, out2,
+                            res_in_place)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(res_out, res_in_place)
+    x = orc.combine(b.y.float().cpu().numpy(), b.pair_slot.cpu().numpy(), b.w.cpu().numpy(), wl.T, wl.k, wl.shared)
+    s_ref, out_ref = orc.add_rmsnorm(x, workloads.bits(residual), workloads.bits(weight), eps)
+    got_s = res_out.double().cpu().numpy()
+    got = out.double().cpu().numpy()
+    # bf16 rounding of the stored value (<= 2^-9 relative) plus fp32 vs double arithmetic
+    assert np.all(np.abs(got_s - s_ref) <= 2.0 ** -8 * np.abs(s_ref) + 1e-6 * np.abs(s_ref).max())
+    assert np.all(np.abs(got - out_ref) <= 2.0 ** -8 * np.abs(out_ref) + 1e-6 * np.abs(out_ref).max())
+    log(f"  combine+rmsnorm: max|out-ref| {np.abs(got - out_ref).max():.3e}, max|ref| {np.abs(out_ref).max():.3e}")
