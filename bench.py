@@ -1,15 +1,20 @@
 """Benchmark of the fused MoE layer forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|mxfp8|router|tiny]
-                    [--launch graph|eager]
+                    [--launch graph|eager] [--chain stages|persistent]
 
 A step is one pass of the whole chain (route -> align -> [quant] -> Gate-Up ->
 Down -> combine; router GEMM first for the router workload) over one batch of
 seeded synthetic input already resident in HBM.  The timed steps are eager
 launches on one stream with nothing else in between (with --launch graph the
 chain is captured once as a HIP graph and every step is one replay; on
-MI355X that measured no faster).  A separate pass with HIP events around
-every stage gives the per-kernel times.  Prints ONE JSON line.
+MI355X that measured no faster).  With --chain persistent a step is one
+moe_forward_persistent call instead: the same stages as phases of one
+persistent kernel chained by device-side ready flags.  Where that entry point
+applies (bf16 weights, T*k <= 16*E) both chains are timed and reported under
+layer.chain_ms, and their outputs are compared bit for bit.  A separate pass
+with HIP events around every stage gives the per-kernel times.  Prints ONE
+JSON line.
 
 value = tokens per second of the whole layer (T tokens per step).  The
 roofline object describes the dominant kernel (the Gate-Up GEMM): its
@@ -155,6 +160,8 @@ def main():
                     help="fuse a residual add + RMSNorm into the combine stage (bf16 residual and weight)")
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
                     help="time the chain as eager launches (default) or as one captured HIP graph per step")
+    ap.add_argument("--chain", choices=("stages", "persistent"), default="stages",
+                    help="a step is the five-stage chain (default) or one moe_forward_persistent call")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, run a plain device copy of BYTES bytes 5 times (used to scale "
@@ -223,34 +230,61 @@ def main():
 
     # whole-chain steps: eager launches, or the chain captured once as a HIP
     # graph and replayed (the kernels and buffers are the same)
-    if args.launch == "graph":
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            run_chain(layer, b, d["x"], wl.k, **kw)
-        stream.wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            run_chain(layer, b, d["x"], wl.k, **kw)
-        graph.replay()
-        step = graph.replay
-    else:
-        def step():
-            run_chain(layer, b, d["x"], wl.k, **kw)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps ({args.launch})")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
+    def timed(fn, label):
+        if args.launch == "graph":
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                fn()
+            stream.wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            graph.replay()
+            step = graph.replay
+        else:
+            step = fn
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        log(f"[bench] timing {args.steps} steps ({label}, {args.launch})")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(end) / args.steps, wall * 1e3 / args.steps
+
+    pers_ok = wl.wtype == "bf16" and wl.T * wl.k <= 16 * wl.E and not args.residual_norm
+    if args.chain == "persistent" and not pers_ok:
+        print("--chain persistent needs bf16 weights, T*k <= 16*E and no --residual-norm", file=sys.stderr)
+        sys.exit(2)
+    chain_ms = {}
+    pers_same = None
+    if pers_ok:
+        ydt = moe.MOE_DTYPE_F32 if y_dtype == torch.float32 else moe.MOE_DTYPE_BF16
+        pws = torch.empty(moe.moe_forward_workspace_bytes(layer.experts, wl.T, wl.k, ydt), dtype=torch.uint8,
+                          device=dev)
+        pout = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+        def persistent():
+            moe.moe_forward_persistent(layer.experts, d["x"], wl.k, pout, pws, logits=kw["logits"], router_hi=hi,
+                                       router_lo=lo, bias=d["bias"], bias_rows=d["bias_rows"], y_dtype=ydt)
+        for _ in range(args.warmup):
+            persistent()
+        chain_ms["persistent"], pers_wall = timed(persistent, "persistent")
+        moe.moe_forward_persistent_status(pws)
+    chain_ms["stages"], stages_wall = timed(lambda: run_chain(layer, b, d["x"], wl.k, **kw), "stages")
+    if pers_ok:
+        pers_same = bool(torch.equal(pout, b.out))
+        if not pers_same:
+            log("[bench] WARNING: persistent chain output differs from the five-stage chain")
+    ms_step = chain_ms[args.chain]
+    wall_ms = pers_wall if args.chain == "persistent" else stages_wall
     log("[bench] per-stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()) +
-        f"; step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms, {args.launch})")
+        f"; step {ms_step:.4f} ms (wall {wall_ms:.4f} ms, {args.chain}, {args.launch})" +
+        (f"; persistent {chain_ms['persistent']:.4f} ms, stages {chain_ms['stages']:.4f} ms" if pers_ok else ""))
 
     value = wl.T / (ms_step * 1e-3)
     g13_bytes, g13_flops, touched = gemm13_algorithmic(wl, counts)
@@ -274,7 +308,7 @@ def main():
                   "hbm_floor_gbs": floor / (ms_step * 1e-3) / 1e9,
                   "hbm_frac": floor / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "mfma_frac": lf / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["fp8" if fp8 else "bf16"],
-                  "stage_ms": stage_ms}
+                  "stage_ms": stage_ms, "chain_ms": chain_ms, "persistent_matches_stages": pers_same}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -291,7 +325,7 @@ def main():
            "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
                       "shared": wl.shared, "weights": wl.wtype, "router": wl.router,
                       "y_dtype": "f32" if y_dtype == torch.float32 else "bf16", "seed": wl.seed,
-                      "launch": args.launch, "residual_norm": bool(args.residual_norm)},
+                      "launch": args.launch, "chain": args.chain, "residual_norm": bool(args.residual_norm)},
            "roofline": roof, "layer": layer_info, "cpu_baseline": cpu,
            "kernel_source_hash": src_hash}
     print(json.dumps(rec), flush=True)

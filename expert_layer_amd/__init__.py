@@ -64,6 +64,9 @@ _SIGS = {
     "moe_combine_rmsnorm": (_I32, [_P, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _P, ctypes.c_float, _P, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [ctypes.POINTER(moe_experts_t), _I64, _I32, _I32]),
     "moe_forward": (_I32, [ctypes.POINTER(moe_experts_t), ctypes.POINTER(moe_forward_args_t), _P, _SZ, _P]),
+    "moe_forward_persistent": (_I32, [ctypes.POINTER(moe_experts_t), ctypes.POINTER(moe_forward_args_t), _P, _SZ,
+                                      _P]),
+    "moe_forward_persistent_status": (_I32, [_P, _P]),
 }
 
 _lib = None
@@ -274,3 +277,19 @@ def moe_forward(ex: Experts, x, k, out, ws, logits=None, router_hi=None, router_
                               _ptr(bias_rows), _ptr(out), _ptr(topk_ids), _ptr(topk_w))
     nbytes = ws.numel() * ws.element_size()
     _check(lib().moe_forward(ex.ref, ctypes.byref(args), _ptr(ws), nbytes, _stream(x)), "moe_forward")
+
+
+def moe_forward_persistent(ex: Experts, x, k, out, ws, logits=None, router_hi=None, router_lo=None, bias=None,
+                           bias_rows=None, y_dtype=MOE_DTYPE_F32, topk_ids=None, topk_w=None):
+    """moe_forward as one persistent kernel with device-side ready flags."""
+    T = x.shape[0]
+    args = moe_forward_args_t(T, k, y_dtype, _ptr(x), _ptr(logits), _ptr(router_hi), _ptr(router_lo), _ptr(bias),
+                              _ptr(bias_rows), _ptr(out), _ptr(topk_ids), _ptr(topk_w))
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().moe_forward_persistent(ex.ref, ctypes.byref(args), _ptr(ws), nbytes, _stream(x)),
+           "moe_forward_persistent")
+
+
+def moe_forward_persistent_status(ws):
+    """Waits for the stream; raises if the last persistent call on ws timed out on the device."""
+    _check(lib().moe_forward_persistent_status(_ptr(ws), _stream(ws)), "moe_forward_persistent_status")

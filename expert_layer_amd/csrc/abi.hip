@@ -362,7 +362,7 @@ int moe_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, co
 namespace {
 
 struct FwdLayout {
-  size_t logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, gemm_ws, xq, xs, h, hs, y, total;
+  size_t ctl, logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, gemm_ws, xq, xs, h, hs, y, total;
 };
 
 FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype, bool router) {
@@ -376,6 +376,9 @@ FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype,
     off += round_up(n);
     return at;
   };
+  // control words of the persistent chain first, so that
+  // moe_forward_persistent_status finds them at offset 0
+  L.ctl = take((size_t)chain_ctl_ints(ex->E, ex->has_shared, T, k) * 4);
   L.logits = take(router ? (size_t)T * ex->E * 4 : 0);
   L.ids = take((size_t)P * 4);
   L.w = take((size_t)P * 4);
@@ -401,8 +404,15 @@ size_t moe_forward_workspace_bytes(const moe_experts_t* ex, int64_t T, int k, in
   return forward_layout(ex, T, k, y_dtype, true).total;
 }
 
-int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, void* stream) {
-  MOE_GUARD_BEGIN
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by moe_forward and moe_forward_persistent.  On
+// MOE_OK with T > 0, *L is the workspace layout.
+int check_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, FwdLayout* L,
+                  bool* empty) {
+  *empty = false;
   if (!args) return MOE_EINVAL;
   int st = check_experts(ex);
   if (st != MOE_OK) return st;
@@ -414,15 +424,34 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   const bool router = args->logits == nullptr;
   if (router && (!args->router_hi || !args->router_lo)) return MOE_EINVAL;
   if (args->bias_rows && !args->bias) return MOE_EINVAL;
-  if (T == 0) return MOE_OK;
+  if (T == 0) {
+    *empty = true;
+    return MOE_OK;
+  }
   if (!args->x || !args->out) return MOE_EINVAL;
   if (!aligned16(args->x) || !aligned16(args->out)) return MOE_EINVAL;
   if (router && (!aligned16(args->router_hi) || !aligned16(args->router_lo))) return MOE_EINVAL;
   // the workspace always has room for the logits, matching moe_forward_workspace_bytes
-  const FwdLayout L = forward_layout(ex, T, k, args->y_dtype, true);
-  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
-  if (overlap(ws, L.total, args->out, (size_t)T * ex->H * 2) || overlap(ws, L.total, args->x, (size_t)T * ex->H * 2))
+  *L = forward_layout(ex, T, k, args->y_dtype, true);
+  if (ws == nullptr || ws_bytes < L->total) return MOE_EWORKSPACE;
+  if (overlap(ws, L->total, args->out, (size_t)T * ex->H * 2) || overlap(ws, L->total, args->x, (size_t)T * ex->H * 2))
     return MOE_EINVAL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, void* stream) {
+  MOE_GUARD_BEGIN
+  FwdLayout L;
+  bool empty;
+  const int st = check_forward(ex, args, ws, ws_bytes, &L, &empty);
+  if (st != MOE_OK || empty) return st;
+  const int64_t T = args->T;
+  const int k = args->k;
+  const bool router = args->logits == nullptr;
 
   char* base = static_cast<char*>(ws);
   hipStream_t s = (hipStream_t)stream;
@@ -475,6 +504,59 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   if (e != hipSuccess) return MOE_EDEVICE;
   e = launch_combine(y, args->y_dtype, pair_slot, w, T, k, ex->H, ex->has_shared, args->out, s);
   return device_status(e);
+  MOE_GUARD_END
+}
+
+int moe_forward_persistent(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes,
+                           void* stream) {
+  MOE_GUARD_BEGIN
+  FwdLayout L;
+  bool empty;
+  int st = check_forward(ex, args, ws, ws_bytes, &L, &empty);
+  if (st != MOE_OK || empty) return st;
+  const int64_t T = args->T;
+  const int k = args->k;
+  if (ex->wtype != MOE_W_BF16) return MOE_EUNSUPPORTED;
+  char* base = static_cast<char*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* slot_pair = reinterpret_cast<int32_t*>(base + L.slot_pair);
+  const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
+  if (!chain_supported(a)) return MOE_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const bool router = args->logits == nullptr;
+  float* logits = router ? reinterpret_cast<float*>(base + L.logits) : nullptr;
+  if (router) {
+    const hipError_t e = launch_router_gemm(args->x, args->router_hi, args->router_lo, logits, T, ex->H, ex->E, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+  }
+  ChainBuffers b;
+  b.logits = router ? logits : args->logits;
+  b.bias = args->bias;
+  b.bias_rows = args->bias_rows;
+  b.x = args->x;
+  b.ids = args->topk_ids ? args->topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
+  b.w = args->topk_w ? args->topk_w : reinterpret_cast<float*>(base + L.w);
+  b.counts = reinterpret_cast<int32_t*>(base + L.counts);
+  b.offsets = offsets;
+  b.slot_pair = slot_pair;
+  b.pair_slot = reinterpret_cast<int32_t*>(base + L.pair_slot);
+  b.h = reinterpret_cast<uint16_t*>(base + L.h);
+  b.y = base + L.y;
+  b.y_dtype = args->y_dtype;
+  b.out = args->out;
+  b.ctl = reinterpret_cast<int*>(base + L.ctl);
+  return device_status(launch_chain(a, b, s));
+  MOE_GUARD_END
+}
+
+int moe_forward_persistent_status(const void* ws, void* stream) {
+  MOE_GUARD_BEGIN
+  if (ws == nullptr) return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  int words[kChainCtlInts];
+  if (hipMemcpyAsync(words, ws, sizeof(words), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_EDEVICE;
+  return words[3] != 0 ? MOE_EDEVICE : MOE_OK;
   MOE_GUARD_END
 }
 

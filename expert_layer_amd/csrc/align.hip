@@ -27,23 +27,6 @@ constexpr int kChunk = 8192;
 constexpr int kSeg = kChunk / kWaves;  // pairs per wave segment (multiple of 64)
 constexpr int kMaxE = 1024;
 
-// Lanes of this wave whose value equals mine, for values in [0, 2^bits).
-__device__ __forceinline__ uint64_t match_lanes(int v, int bits) {
-  uint64_t m = ~0ull;
-  for (int b = 0; b < bits; ++b) {
-    const bool set = (v >> b) & 1;
-    const uint64_t bal = __ballot(set);
-    m &= set ? bal : ~bal;
-  }
-  return m;
-}
-
-__device__ __forceinline__ int id_bits(int E) {
-  int bits = 1;
-  while ((1 << bits) < E + 1) ++bits;  // room for the sentinel value E
-  return bits;
-}
-
 // wcnt[w][e] (LDS) := number of pairs of expert e in wave w's segment.
 __device__ void count_segments(const int32_t* __restrict__ ids, int64_t P, int64_t chunk0, int E,
                                int* wcnt) {

@@ -1,0 +1,55 @@
+// Fixed-order top-k weighted sum of one token's expert outputs, 8 columns
+// at a time (HPC-Ops page, FusedMoE stage 5): j ascending with fp32 fma,
+// then the shared expert added, no atomics.  Shared by the combine kernels
+// and the persistent chain.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe355 {
+
+// y terms of one token for 8 columns starting at c, summed in fixed order
+template <int YBF16>
+__device__ __forceinline__ void combine8(const void* __restrict__ yv, const int32_t* slot, const float* wt,
+                                         int nterm, int k, int64_t P, int64_t t, int H, int c, float acc[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < nterm; ++j) {
+    const bool sh = j == k;
+    const int64_t s = sh ? P + t : (int64_t)slot[j];
+    const float a = sh ? 1.0f : wt[j];
+    float v[8];
+    if (YBF16) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yv) + s * H + c);
+      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(u[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(yv) + s * H + c);
+      const float4 a0 = p[0], a1 = p[1];
+      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    }
+    if (sh) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(a, v[i], acc[i]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float v[8]) {
+  uint4 o;
+  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+  o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+  return o;
+}
+
+}  // namespace moe355

@@ -57,6 +57,23 @@ __device__ __forceinline__ float wave_max16(float v) {
   return v;
 }
 
+// Lanes of this wave whose value equals mine, for values in [0, 2^bits).
+__device__ __forceinline__ uint64_t match_lanes(int v, int bits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < bits; ++b) {
+    const bool set = (v >> b) & 1;
+    const uint64_t bal = __ballot(set);
+    m &= set ? bal : ~bal;
+  }
+  return m;
+}
+
+__device__ __forceinline__ int id_bits(int E) {
+  int bits = 1;
+  while ((1 << bits) < E + 1) ++bits;  // room for the sentinel value E
+  return bits;
+}
+
 // ------------------------------------------------------------------ launchers
 // All launchers enqueue on `s` and return hipGetLastError().  Shapes have been
 // validated by the ABI layer.
@@ -120,6 +137,29 @@ hipError_t launch_gemm13_fp8_tiled(const GemmArgs& a, const uint8_t* xq, const f
                                    hipStream_t s);
 hipError_t launch_gemm2_fp8_tiled(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
                                   hipStream_t s);
+
+// Persistent chain (route .. combine in one launch, device-side ready flags).
+// ctl: control area of chain_ctl_ints() ints, owned by the caller.
+constexpr int kChainCtlInts = 16;
+struct ChainBuffers {
+  const float* logits;
+  const float* bias;
+  const uint8_t* bias_rows;
+  const uint16_t* x;
+  int32_t *ids, *counts, *offsets, *slot_pair, *pair_slot;
+  float* w;
+  uint16_t* h;
+  void* y;
+  int y_dtype;
+  uint16_t* out;
+  int* ctl;
+};
+int64_t chain_max_chunks(int E, int has_shared, int64_t T, int k);
+inline int64_t chain_ctl_ints(int E, int has_shared, int64_t T, int k) {
+  return kChainCtlInts + 6 * chain_max_chunks(E, has_shared, T, k) + E + 2;
+}
+bool chain_supported(const GemmArgs& a);
+hipError_t launch_chain(const GemmArgs& a, const ChainBuffers& b, hipStream_t s);
 
 hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
                           int k, int H, int has_shared, uint16_t* out, hipStream_t s);

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE355_ABI_VERSION 2
+#define MOE355_ABI_VERSION 3
 
 enum {
   MOE_OK = 0,
@@ -254,6 +254,30 @@ typedef struct moe_forward_args_t {
 size_t moe_forward_workspace_bytes(const moe_experts_t* ex, int64_t T, int k, int y_dtype);
 int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* ------------------------------------------------------------------ the chain in one launch
+ * Same arguments, workspace and result as moe_forward, bitwise: the stages run
+ * as phases of one persistent kernel that hands out work items in chain order
+ * from a counter in the workspace and signals readiness through device-side
+ * counters (route -> align -> each 16-row chunk's Gate-Up tiles -> that
+ * chunk's Down tiles -> each token's combine), the single-launch analogue of
+ * the HPC-Ops page's PDL-chained FusedMoE stages (main functions: FusedMoE;
+ * technical principles: PDL).  A Down tile fetches its first weight stages
+ * before it waits for its h rows.  Enqueues a small clear kernel, then the
+ * chain kernel ([router_gemm] first when logits is NULL).
+ * Envelope: wtype MOE_W_BF16 and at most 16 routed rows per expert on average
+ * (T*k <= 16*E); anything else returns MOE_EUNSUPPORTED with nothing enqueued.
+ * Two calls that share a workspace must not run concurrently.
+ */
+int moe_forward_persistent(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Waits for `stream`, then reports whether the last moe_forward_persistent
+ * call on workspace `ws` completed: MOE_OK, or MOE_EDEVICE when a device-side
+ * wait ran out of time (about half a second; it means a device fault or a
+ * bug, and out is then undefined).  MOE_EINVAL for a NULL workspace.
+ */
+int moe_forward_persistent_status(const void* ws, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,14 +34,14 @@ def L():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert sorted(moe.exported_symbols()) == names
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert moe.moe_status_string(0) == "ok"
     for s in range(1, 5):
         assert moe.moe_status_string(s) not in ("ok", "unknown status")
@@ -180,6 +180,34 @@ def test_forward_validation(L):
     assert L.moe_forward(ctypes.byref(ex), None, ws, need, None) == moe.MOE_EINVAL
     args0 = moe.moe_forward_args_t(0, 2, 0, None, B, None, None, None, None, None, None, None)
     assert L.moe_forward(ctypes.byref(ex), ctypes.byref(args0), None, 0, None) == moe.MOE_OK
+
+
+def test_forward_persistent_validation(L):
+    """Same argument rules as moe_forward, plus the envelope (bf16 weights, T*k <= 16*E);
+    every call here stops at host validation (or T == 0), so nothing is launched."""
+    fp = L.moe_forward_persistent
+    ex = _experts(has_shared=0)
+    need = L.moe_forward_workspace_bytes(ctypes.byref(ex), 16, 2, 0)
+    ws = 0x40000000
+    args = moe.moe_forward_args_t(16, 2, 0, A, B, None, None, None, None, C, None, None)
+    assert fp(ctypes.byref(ex), ctypes.byref(args), ws, need - 1, None) == moe.MOE_EWORKSPACE
+    assert fp(ctypes.byref(ex), ctypes.byref(args), None, need, None) == moe.MOE_EWORKSPACE
+    args2 = moe.moe_forward_args_t(16, 2, 0, A, None, None, None, None, None, C, None, None)
+    assert fp(ctypes.byref(ex), ctypes.byref(args2), ws, need, None) == moe.MOE_EINVAL   # no logits, no router
+    args3 = moe.moe_forward_args_t(16, 2, 5, A, B, None, None, None, None, C, None, None)
+    assert fp(ctypes.byref(ex), ctypes.byref(args3), ws, need, None) == moe.MOE_EUNSUPPORTED
+    assert fp(ctypes.byref(ex), None, ws, need, None) == moe.MOE_EINVAL
+    assert fp(ctypes.byref(ex), ctypes.byref(args), C, need, None) == moe.MOE_EINVAL     # workspace holds out
+    # outside the envelope: fp8 weights, and more than 16 routed rows per expert on average
+    ex8 = _experts(wtype=1, s1=D, s3=D, s2=D)
+    need8 = L.moe_forward_workspace_bytes(ctypes.byref(ex8), 16, 2, 0)
+    assert fp(ctypes.byref(ex8), ctypes.byref(args), ws, need8, None) == moe.MOE_EUNSUPPORTED
+    big = moe.moe_forward_args_t(128, 2, 0, A, B, None, None, None, None, C, None, None)   # 256 > 16 * 8 rows
+    need_big = L.moe_forward_workspace_bytes(ctypes.byref(ex), 128, 2, 0)
+    assert fp(ctypes.byref(ex), ctypes.byref(big), ws, need_big, None) == moe.MOE_EUNSUPPORTED
+    args0 = moe.moe_forward_args_t(0, 2, 0, None, B, None, None, None, None, None, None, None)
+    assert fp(ctypes.byref(ex), ctypes.byref(args0), None, 0, None) == moe.MOE_OK
+    assert L.moe_forward_persistent_status(None, None) == moe.MOE_EINVAL
 
 
 def test_router_validation(L):
