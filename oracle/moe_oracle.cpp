@@ -37,6 +37,14 @@
 //    power of two), clamped to [-127, 127]; an all-zero block uses X = -127;
 //    elements are E4M3FN codes of v * 2^-X, rounded to nearest even and
 //    saturated at 448.
+//  * per-tensor FP8 (the second FP8 mode the HPC-Ops page lists for its
+//    GroupGEMM, main functions): one fp32 scale per tensor, amax / 448 as for
+//    a block (1 if amax = 0).  Each expert weight matrix is a tensor; x is one
+//    tensor [T, H]; h is one tensor over all of its [R, I] values, quantised
+//    from h rounded to fp32 after the whole Gate-Up is known (a per-tensor
+//    scale needs the amax of the whole tensor before any code).  Products of
+//    codes are summed over the whole K and scaled once by (activation scale
+//    x weight scale).
 //
 // Parity pins for every function here live in tests/test_oracle_*.py.
 
@@ -299,6 +307,24 @@ void orc_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, u
   });
 }
 
+// Per-tensor quantisation (HPC-Ops page, main functions: GroupGEMM FP8 with
+// per-tensor scales): mats tensors of n values each, bf16 bit patterns
+// (f32 = 0) or fp32 values (f32 = 1).  s[m] = amax / 448 (fp32, 1 if amax is
+// 0), q = e4m3(fp32(v / s[m])).
+void orc_quant_tensor_fp8(const void* x, int f32, int64_t mats, int64_t n, uint8_t* q, float* s) {
+  auto val = [&](int64_t i) -> float {
+    if (f32) return static_cast<const float*>(x)[i];
+    return static_cast<float>(bf16_value(static_cast<const uint16_t*>(x)[i]));
+  };
+  for (int64_t m = 0; m < mats; ++m) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) amax = std::max(amax, std::fabs(val(m * n + i)));
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    s[m] = sc;
+    for (int64_t i = 0; i < n; ++i) q[m * n + i] = e4m3_code(val(m * n + i) / sc);
+  }
+}
+
 // ---------------------------------------------------------------- expert FFN
 // One SwiGLU expert on one token, bf16 operands, everything else in double:
 // g = x.w1^T, u = x.w3^T, h = SiLU(g) * u, y = h.w2^T.
@@ -362,6 +388,15 @@ static double mx_dot(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, co
   return acc;
 }
 
+// Per-tensor fp8 dot product of code rows: sum_k dec(xq[k]) * dec(wq[k]) over
+// the whole K (the scales multiply the result once).
+static double tensor_dot(const uint8_t* xq, const uint8_t* wq, int K) {
+  const double* dec = e4m3_table();
+  double acc = 0.0;
+  for (int i = 0; i < K; ++i) acc += dec[xq[i]] * dec[wq[i]];
+  return acc;
+}
+
 // One SwiGLU expert on one token with FP8 operands (the "activation
 // quantisation" stage of FusedMoE between Gate-Up and Down):
 //  xq [H] e4m3 + xs [H/128]; w1q, w3q [I, H] e4m3 + s1, s3 [I/128, H/128];
@@ -402,15 +437,20 @@ void orc_expert_fp8(const uint8_t* xq, const float* xs, const uint8_t* w1q, cons
 // ---------------------------------------------------------------- layer
 // Expert weights for the layer.  bf16 weights (wtype 0), e4m3 codes with
 // 128x128 fp32 block scales (wtype 1: s1, s3 [E, I/128, H/128], s2
-// [E, H/128, I/128]) or MXFP8 (wtype 2: E8M0 bytes per weight row per 32 K,
-// s1, s3 [E, I, H/32], s2 [E, H, I/32]).  Routed experts are [E, ...]; the
-// shared expert (has_shared) is a single expert of the same shape.
+// [E, H/128, I/128]), MXFP8 (wtype 2: E8M0 bytes per weight row per 32 K,
+// s1, s3 [E, I, H/32], s2 [E, H, I/32]) or per-tensor FP8 (wtype 3: one fp32
+// scale per matrix, s1, s3, s2 [E] and ss1, ss3, ss2 [1]).  Routed experts are
+// [E, ...]; the shared expert (has_shared) is a single expert of the same
+// shape.  For wtype 3, h_scale gives the scale of the whole h tensor; when it
+// is NULL the h of the pairs being computed is taken as the whole tensor
+// (exact when every token is computed).
 struct orc_layer {
   int wtype, E, H, I, has_shared;
   const void *w1, *w3, *w2;
   const void *s1, *s3, *s2;
   const void *sw1, *sw3, *sw2;
   const void *ss1, *ss3, *ss2;
+  const float* h_scale;  // per-tensor FP8 only: scale of the whole h, or NULL
 };
 
 // The whole layer on a list of tokens ("top-k weighted combine", stage 5):
@@ -418,7 +458,9 @@ struct orc_layer {
 // bf16 path: x is bf16 [T,H] and xs is NULL.  fp8 path: x is the e4m3 code
 // array [T,H] and xs [T,H/128] its fp32 scales (from orc_quant_rows_fp8).
 // MXFP8 path: x codes [T,H] and xs [T,H/32] E8M0 bytes (orc_quant_rows_mx);
-// h is requantised per row per 32 columns with the MX rule.
+// h is requantised per row per 32 columns with the MX rule.  Per-tensor FP8:
+// x codes [T,H] and xs [1] (orc_quant_tensor_fp8 of the whole x); h is
+// requantised with one scale (L->h_scale, or from these pairs' h).
 // ids / weights are the route output [T,k].  out: [nrows, H] double.
 //
 // The arithmetic per (token, expert) is exactly orc_expert_bf16 /
@@ -435,6 +477,7 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
   const int64_t npairs = nrows * per_row;
   const bool fp8 = L->wtype != 0;
   const bool mx = L->wtype == 2;
+  const bool pt = L->wtype == 3;
   const int hm = H / 32, im = I / 32;   // MX blocks per row
   auto fs = [](const void* p) { return static_cast<const float*>(p); };
   auto bs = [](const void* p) { return static_cast<const uint8_t*>(p); };
@@ -451,7 +494,8 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
 
   std::vector<double> hbuf(npairs * (int64_t)I);   // h per pair (double; fp8: fp32-rounded)
   std::vector<uint8_t> hq(fp8 ? npairs * (int64_t)I : 0);
-  std::vector<float> hs(fp8 && !mx ? npairs * (int64_t)ib : 0);
+  std::vector<float> hs(fp8 && !mx && !pt ? npairs * (int64_t)ib : 0);
+  float h_tensor_scale = 1.0f;
   std::vector<uint8_t> hsm(mx ? npairs * (int64_t)im : 0);
   std::vector<double> ybuf(npairs * (int64_t)H);
 
@@ -488,6 +532,12 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
             const uint8_t* s3 = sh ? bs(L->ss3) + (int64_t)n * hm : bs(L->s3) + ((int64_t)g * I + n) * hm;
             gv = mx_dot(xr, xsr, w1, s1, H);
             uv = mx_dot(xr, xsr, w3, s3, H);
+          } else if (pt) {
+            const double xsc = fs(xs)[0];
+            const double s1 = sh ? fs(L->ss1)[0] : fs(L->s1)[g];
+            const double s3 = sh ? fs(L->ss3)[0] : fs(L->s3)[g];
+            gv = tensor_dot(xr, w1, H) * xsc * s1;
+            uv = tensor_dot(xr, w3, H) * xsc * s3;
           } else {
             const float* xsr = fs(xs) + t * hb;
             const float* s1 = (sh ? fs(L->ss1) : fs(L->s1) + g * blk) + (n / 128) * hb;
@@ -509,8 +559,22 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
       for (int b = 0; b < im; ++b) mx_quant_block(hv.data() + b * 32, 32, &hq[q * I + b * 32], &hsm[q * im + b]);
     });
   }
+  // per-tensor fp8: one scale for the whole fp32-rounded h
+  if (pt) {
+    if (L->h_scale) {
+      h_tensor_scale = *L->h_scale;
+    } else {
+      float amax = 0.0f;
+      for (int64_t i = 0; i < npairs * (int64_t)I; ++i) amax = std::max(amax, std::fabs(static_cast<float>(hbuf[i])));
+      h_tensor_scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+    const float sc = h_tensor_scale;
+    parallel_for(npairs, nthreads, [&](int64_t q) {
+      for (int i = 0; i < I; ++i) hq[q * I + i] = e4m3_code(static_cast<float>(hbuf[q * I + i]) / sc);
+    });
+  }
   // fp8: requantise each pair's h per 128 columns (scale amax/448)
-  if (fp8 && !mx) {
+  if (fp8 && !mx && !pt) {
     parallel_for(npairs, nthreads, [&](int64_t q) {
       for (int gi = 0; gi < ib; ++gi) {
         float amax = 0.0f;
@@ -541,6 +605,9 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
           if (mx) {
             const uint8_t* s2 = sh ? bs(L->ss2) + (int64_t)m * im : bs(L->s2) + ((int64_t)g * H + m) * im;
             acc = mx_dot(hq.data() + q * I, hsm.data() + q * im, w2, s2, I);
+          } else if (pt) {
+            const double s2 = sh ? fs(L->ss2)[0] : fs(L->s2)[g];
+            acc = tensor_dot(hq.data() + q * I, w2, I) * static_cast<double>(h_tensor_scale) * s2;
           } else {
             const float* s2 = (sh ? fs(L->ss2) : fs(L->s2) + g * blk) + (m / 128) * ib;
             acc = fp8_dot(hq.data() + q * I, hs.data() + q * ib, w2, s2, I);

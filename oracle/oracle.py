@@ -39,7 +39,8 @@ def build() -> str:
 class _Layer(ctypes.Structure):
     _fields_ = [("wtype", _I32), ("E", _I32), ("H", _I32), ("I", _I32), ("has_shared", _I32),
                 ("w1", _P), ("w3", _P), ("w2", _P), ("s1", _P), ("s3", _P), ("s2", _P),
-                ("sw1", _P), ("sw3", _P), ("sw2", _P), ("ss1", _P), ("ss3", _P), ("ss2", _P)]
+                ("sw1", _P), ("sw3", _P), ("sw2", _P), ("ss1", _P), ("ss3", _P), ("ss2", _P),
+                ("h_scale", _P)]
 
 
 _lib = None
@@ -70,6 +71,7 @@ def lib():
         L.orc_quant_rows_mx.argtypes = [_P, _I64, _I32, _P, _P, _I32]
         L.orc_quant_rows_mx_f32.argtypes = [_P, _I64, _I32, _P, _P]
         L.orc_quant_blocks_fp8.argtypes = [_P, _I64, _I32, _I32, _P, _P, _I32]
+        L.orc_quant_tensor_fp8.argtypes = [_P, _I32, _I64, _I64, _P, _P]
         L.orc_expert_bf16.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_expert_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_layer_rows.argtypes = [ctypes.POINTER(_Layer), _P, _P, _P, _P, _I32, _P, _I64, _P, _I32]
@@ -201,6 +203,18 @@ def quant_blocks_fp8(w_bits, nthreads=None):
     return (q[0], s[0]) if squeeze else (q, s)
 
 
+def quant_tensor_fp8(x, mats=1):
+    """Per-tensor FP8 of ``mats`` equal parts of x (bf16 bit patterns as uint16,
+    or fp32 values): codes shaped like x and one fp32 scale per part [mats]."""
+    f32 = x.dtype == np.float32
+    x = _c(x, np.float32 if f32 else np.uint16)
+    n = x.size // mats
+    q = np.empty(x.shape, np.uint8)
+    s = np.empty(mats, np.float32)
+    lib().orc_quant_tensor_fp8(_ptr(x), int(f32), mats, n, _ptr(q), _ptr(s))
+    return q, s
+
+
 # ------------------------------------------------------------------ experts / layer
 def expert_bf16(x_bits, w1, w3, w2):
     x_bits, w1, w3, w2 = (_c(a, np.uint16) for a in (x_bits, w1, w3, w2))
@@ -231,10 +245,13 @@ class Layer:
     s1, s3 [E, I/128, H/128], s2 [E, H/128, I/128] (and ss1/ss3/ss2).
     MXFP8: ``wtype=2``, uint8 codes and uint8 E8M0 scales per weight row per
     32 K: s1, s3 [E, I, H/32], s2 [E, H, I/32] (and the shared ones).
+    Per-tensor FP8: ``wtype=3``, uint8 codes and one fp32 scale per matrix,
+    s1, s3, s2 [E] and ss1, ss3, ss2 [1]; ``h_scale`` fixes the scale of the
+    whole h (None: computed from the h of the rows evaluated).
     """
 
     def __init__(self, w1, w3, w2, sw1=None, sw3=None, sw2=None, wtype=0,
-                 s1=None, s3=None, s2=None, ss1=None, ss3=None, ss2=None):
+                 s1=None, s3=None, s2=None, ss1=None, ss3=None, ss2=None, h_scale=None):
         dt = np.uint16 if wtype == 0 else np.uint8
         self.arrays = {}
         for name, a in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
@@ -246,9 +263,10 @@ class Layer:
         self.E, self.I, self.H, self.wtype = E, I, H, wtype
         self.has_shared = sw1 is not None
         a = self.arrays
+        self.arrays["h_scale"] = None if h_scale is None else np.array([h_scale], np.float32)
         self.c = _Layer(wtype, E, H, I, int(self.has_shared),
                         *(_ptr(a[n]) for n in ("w1", "w3", "w2", "s1", "s3", "s2",
-                                               "sw1", "sw3", "sw2", "ss1", "ss3", "ss2")))
+                                               "sw1", "sw3", "sw2", "ss1", "ss3", "ss2", "h_scale")))
 
 
 def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None):
