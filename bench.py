@@ -1,6 +1,6 @@
 """Benchmark of the fused MoE layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|mxfp8|router|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|fp8|mxfp8|fp8t|router|tiny]
                     [--launch graph|eager] [--chain stages|persistent]
 
 A step is one pass of the whole chain (route -> align -> [quant] -> Gate-Up ->
@@ -64,11 +64,12 @@ def gemm13_algorithmic(wl, counts):
 
     bytes: w1 + w3 of every expert with at least one row (plus the shared
     expert), one read of each gathered x row per slot, one write of h per slot
-    (fp8: codes + per-128 scales; mxfp8: codes + one scale byte per 32).
+    (fp8: codes + per-128 scales; mxfp8: codes + one scale byte per 32;
+    fp8t: codes, and h unquantised in fp32 since its scale needs all of h).
     flops: 4*H*I per slot row.
     """
     R = wl.T * wl.k + wl.shared * wl.T
-    wb = 1 if wl.wtype in ("fp8", "mxfp8") else 2
+    wb = 1 if wl.wtype in ("fp8", "mxfp8", "fp8t") else 2
     touched = int((counts > 0).sum()) + wl.shared
     weight = touched * 2 * wl.I * wl.H * wb
     if wl.wtype == "fp8":
@@ -77,6 +78,8 @@ def gemm13_algorithmic(wl, counts):
     elif wl.wtype == "mxfp8":
         weight += touched * 2 * wl.I * (wl.H // 32)
         act = R * (wl.H + wl.H // 32) + R * (wl.I + wl.I // 32)
+    elif wl.wtype == "fp8t":
+        act = R * wl.H + R * wl.I * 4
     else:
         act = R * wl.H * 2 + R * wl.I * 2
     flops = 4.0 * wl.H * wl.I * R
@@ -91,7 +94,7 @@ def layer_flops(wl):
 
 
 def layer_floor_bytes(wl, counts):
-    wb = 1 if wl.wtype in ("fp8", "mxfp8") else 2
+    wb = 1 if wl.wtype in ("fp8", "mxfp8", "fp8t") else 2
     touched = int((counts > 0).sum()) + wl.shared
     b = touched * 3 * wl.I * wl.H * wb
     if wl.wtype == "fp8":
@@ -124,7 +127,7 @@ def cpu_baseline(wl, d, b, budget_s):
     logits = workloads.bits(d["logits"]) if not wl.router else workloads.bits(b.logits)
     bias = workloads.bits(d["bias"]) if d["bias"] is not None else None
     bias_rows = workloads.bits(d["bias_rows"]) if d["bias_rows"] is not None else None
-    if wl.wtype in ("fp8", "mxfp8"):
+    if wl.wtype in ("fp8", "mxfp8", "fp8t"):
         return None
     L = orc.Layer(*(workloads.bits(d[n]) if d[n] is not None else None
                     for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")))
@@ -191,9 +194,9 @@ def main():
     torch.cuda.set_device(dev)
     log(f"[bench] workload {wl.name}: generating inputs")
     d = workloads.make_inputs(wl, device=dev)
-    fp8 = wl.wtype in ("fp8", "mxfp8")
+    fp8 = wl.wtype in ("fp8", "mxfp8", "fp8t")
     layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=wl.wtype == "fp8",
-                               mx=wl.wtype == "mxfp8")
+                               mx=wl.wtype == "mxfp8", pt=wl.wtype == "fp8t")
     y_dtype = torch.float32 if wl.T * (wl.k + wl.shared) * wl.H <= (1 << 24) else torch.bfloat16
     b = Buffers(layer, wl.T, wl.k, y_dtype=y_dtype, router=wl.router)
     hi = lo = None
@@ -212,7 +215,7 @@ def main():
 
     stream = torch.cuda.current_stream()
     names = (["router"] if wl.router else []) + ["route", "align"] + (["quant"] if fp8 else []) + \
-        ["gemm13", "gemm2", "combine"]
+        ["gemm13"] + (["hquant"] if wl.wtype == "fp8t" else []) + ["gemm2", "combine"]
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         run_chain(layer, b, d["x"], wl.k, **kw)

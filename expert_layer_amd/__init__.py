@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("MOE355_LIB") or os.path.join(_PKG, "libmoe355.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EDEVICE = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
-MOE_W_BF16, MOE_W_FP8, MOE_W_MXFP8 = 0, 1, 2
+MOE_W_BF16, MOE_W_FP8, MOE_W_MXFP8, MOE_W_FP8_TENSOR = 0, 1, 2, 3
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -57,6 +57,8 @@ _SIGS = {
     "moe_quant_rows_fp8": (_I32, [_P, _I64, _I32, _P, _P, _P]),
     "moe_quant_blocks_fp8": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_quant_rows_mxfp8": (_I32, [_P, _I64, _I32, _P, _P, _P]),
+    "moe_tensor_amax": (_I32, [_P, _I32, _I64, _I64, _P, _P]),
+    "moe_quant_tensor_fp8": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P, _P]),
     "moe_gemm_workspace_bytes": (_SZ, [ctypes.POINTER(moe_experts_t), _I64, _I32]),
     "moe_gemm13": (_I32, [ctypes.POINTER(moe_experts_t), _P, _P, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "moe_gemm2": (_I32, [ctypes.POINTER(moe_experts_t), _P, _P, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]),
@@ -197,6 +199,22 @@ def moe_quant_rows_mxfp8(x, q, s):
     _check(lib().moe_quant_rows_mxfp8(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(x)), "moe_quant_rows_mxfp8")
 
 
+def moe_tensor_amax(x, amax, mats=1):
+    """amax[m] = max |x| over each of ``mats`` equal parts of x (bf16 or fp32)."""
+    _expect(amax, torch.float32, "amax")
+    dt = MOE_DTYPE_F32 if x.dtype == torch.float32 else MOE_DTYPE_BF16
+    _check(lib().moe_tensor_amax(_ptr(x), dt, mats, x.numel() // mats, _ptr(amax), _stream(x)), "moe_tensor_amax")
+
+
+def moe_quant_tensor_fp8(x, amax, q, s, mats=1):
+    """Per-tensor FP8 of ``mats`` equal parts of x: s[m] = amax[m]/448, q = e4m3(x / s[m])."""
+    _expect(amax, torch.float32, "amax")
+    _expect(s, torch.float32, "s")
+    dt = MOE_DTYPE_F32 if x.dtype == torch.float32 else MOE_DTYPE_BF16
+    _check(lib().moe_quant_tensor_fp8(_ptr(x), dt, mats, x.numel() // mats, _ptr(amax), _ptr(q), _ptr(s),
+                                      _stream(x)), "moe_quant_tensor_fp8")
+
+
 # ------------------------------------------------------------------ experts
 class Experts:
     """Holds the tensors of a layer's experts and the matching moe_experts_t.
@@ -206,6 +224,8 @@ class Experts:
           s1, s3 [E,I/128,H/128], s2 [E,H/128,I/128] (ss1, ss3, ss2 for the shared expert).
     mxfp8: codes plus uint8 E8M0 scales per weight row per 32 K: s1, s3 [E,I,H/32],
           s2 [E,H,I/32] (the scale dtype selects the format).
+    per-tensor fp8: codes plus one fp32 scale per matrix, s1, s3, s2 [E] and ss1, ss3, ss2 [1]
+          (one-dimensional scales select the format).
     """
 
     def __init__(self, w1, w3, w2, sw1=None, sw3=None, sw2=None, s1=None, s3=None, s2=None,
@@ -217,7 +237,8 @@ class Experts:
         self.E, self.I, self.H = E, I, H
         self.has_shared = int(sw1 is not None)
         mx = fp8 and s1 is not None and s1.dtype == torch.uint8
-        self.wtype = MOE_W_MXFP8 if mx else MOE_W_FP8 if fp8 else MOE_W_BF16
+        pt = fp8 and s1 is not None and s1.dim() == 1
+        self.wtype = MOE_W_MXFP8 if mx else MOE_W_FP8_TENSOR if pt else MOE_W_FP8 if fp8 else MOE_W_BF16
         p = {n: _ptr(t) for n, t in self.tensors.items()}
         self.c = moe_experts_t(self.wtype, E, H, I, self.has_shared,
                                p["w1"], p["w3"], p["w2"], p["s1"], p["s3"], p["s2"],

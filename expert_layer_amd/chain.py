@@ -16,8 +16,8 @@ import torch
 from . import (Experts, moe_align, moe_align_workspace_bytes, moe_combine, moe_combine_rmsnorm, moe_gemm2,
                moe_gemm13,
                moe_gemm_workspace_bytes,
-               moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_quant_rows_mxfp8, moe_route, moe_router_gemm,
-               moe_router_split)
+               moe_quant_blocks_fp8, moe_quant_rows_fp8, moe_quant_rows_mxfp8, moe_quant_tensor_fp8, moe_route,
+               moe_router_gemm, moe_router_split, moe_tensor_amax)
 
 
 @dataclass
@@ -29,12 +29,31 @@ class Layer:
     I: int
     shared: int
     mx: bool = False   # MXFP8: E8M0 scales per 32 K
+    pt: bool = False   # per-tensor FP8: one fp32 scale per matrix
 
     @staticmethod
-    def from_weights(w1, w3, w2, sw1=None, sw3=None, sw2=None, fp8=False, mx=False):
+    def from_weights(w1, w3, w2, sw1=None, sw3=None, sw2=None, fp8=False, mx=False, pt=False):
         """bf16 weights as given; fp8 quantises them once with 128x128 block
-        scales, mx once with MXFP8 (per weight row per 32 K)."""
+        scales, mx once with MXFP8 (per weight row per 32 K), pt once with one
+        scale per matrix."""
         E, I, H = w1.shape
+        if pt:
+            q = {}
+            for name, w in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
+                if w is None:
+                    q[name] = (None, None)
+                    continue
+                mats = E if w.dim() == 3 else 1
+                w = w.contiguous()
+                amax = torch.empty(mats, dtype=torch.float32, device=w.device)
+                qt = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+                st = torch.empty(mats, dtype=torch.float32, device=w.device)
+                moe_tensor_amax(w, amax, mats=mats)
+                moe_quant_tensor_fp8(w, amax, qt, st, mats=mats)
+                q[name] = (qt, st)
+            ex = Experts(*(q[n][0] for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")),
+                         *(q[n][1] for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")))
+            return Layer(ex, True, E, H, I, int(sw1 is not None), pt=True)
         if mx:
             q = {}
             for name, w in (("w1", w1), ("w3", w3), ("w2", w2), ("sw1", sw1), ("sw3", sw3), ("sw2", sw2)):
@@ -90,7 +109,18 @@ class Buffers:
         self.align_ws = torch.empty(max(nws // 4, 1), **i32)
         gws = moe_gemm_workspace_bytes(layer.experts, T, k)
         self.gemm_ws = torch.empty(max(gws // 4, 1), **i32)
-        if layer.mx:
+        if layer.pt:
+            # x and h each have one amax and one scale; h is kept in fp32 until
+            # its tensor-wide scale is known, then quantised into hq
+            f32 = dict(dtype=torch.float32, device=dev)
+            self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+            self.x_amax = torch.empty(1, **f32)
+            self.xs = torch.empty(1, **f32)
+            self.h = torch.empty((R, I), **f32)
+            self.h_amax = torch.empty(1, **f32)
+            self.hq = torch.empty((R, I), dtype=torch.uint8, device=dev)
+            self.hs = torch.empty(1, **f32)
+        elif layer.mx:
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
             self.xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
             self.h = torch.empty((R, I), dtype=torch.uint8, device=dev)
@@ -139,7 +169,18 @@ def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, route
     moe_align(b.ids, layer.E, layer.shared, b.counts, b.offsets, b.slot_pair, b.pair_slot, b.align_ws)
     ev("align", 1)
     ex = layer.experts
-    if layer.fp8:
+    if layer.pt:
+        ev("quant", 0)
+        moe_tensor_amax(x, b.x_amax)
+        moe_quant_tensor_fp8(x, b.x_amax, b.xq, b.xs)
+        ev("quant", 1)
+        ev("gemm13", 0)
+        moe_gemm13(ex, b.xq, b.xs, b.offsets, b.slot_pair, T, k, b.h, b.h_amax, ws=b.gemm_ws)
+        ev("gemm13", 1)
+        ev("hquant", 0)
+        moe_quant_tensor_fp8(b.h, b.h_amax, b.hq, b.hs)
+        ev("hquant", 1)
+    elif layer.fp8:
         ev("quant", 0)
         if layer.mx:
             moe_quant_rows_mxfp8(x, b.xq, b.xs)
@@ -154,7 +195,7 @@ def run_chain(layer: Layer, b: Buffers, x, k, logits=None, router_hi=None, route
         moe_gemm13(ex, x, None, b.offsets, b.slot_pair, T, k, b.h, ws=b.gemm_ws)
         ev("gemm13", 1)
     ev("gemm2", 0)
-    moe_gemm2(ex, b.h, b.hs, b.offsets, T, k, b.y)
+    moe_gemm2(ex, b.hq if layer.pt else b.h, b.hs, b.offsets, T, k, b.y)
     ev("gemm2", 1)
     ev("combine", 0)
     if residual is None:

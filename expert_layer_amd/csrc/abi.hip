@@ -51,7 +51,9 @@ int check_route_shape(int64_t T, int E, int k) {
 
 int check_experts(const moe_experts_t* ex) {
   if (ex == nullptr) return MOE_EINVAL;
-  if (ex->wtype != MOE_W_BF16 && ex->wtype != MOE_W_FP8 && ex->wtype != MOE_W_MXFP8) return MOE_EUNSUPPORTED;
+  if (ex->wtype != MOE_W_BF16 && ex->wtype != MOE_W_FP8 && ex->wtype != MOE_W_MXFP8 &&
+      ex->wtype != MOE_W_FP8_TENSOR)
+    return MOE_EUNSUPPORTED;
   if (ex->E <= 0 || ex->H <= 0 || ex->I <= 0) return MOE_EINVAL;
   if (ex->has_shared != 0 && ex->has_shared != 1) return MOE_EINVAL;
   if (ex->E > 1024 || ex->H % 128 != 0 || ex->I % 128 != 0) return MOE_EUNSUPPORTED;
@@ -62,13 +64,15 @@ int check_experts(const moe_experts_t* ex) {
   // the MXFP8 Down kernel tiles 256 output columns; its scale rows are read
   // as 4-byte words
   auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-  if (ex->wtype == MOE_W_MXFP8 && ex->H % 256 != 0) return MOE_EUNSUPPORTED;
-  if (ex->wtype == MOE_W_MXFP8 && (!a4(ex->s1) || !a4(ex->s3) || !a4(ex->s2))) return MOE_EINVAL;
+  // the MXFP8 and per-tensor Down kernels tile 256 output columns
+  const bool tiled8 = ex->wtype == MOE_W_MXFP8 || ex->wtype == MOE_W_FP8_TENSOR;
+  if (tiled8 && ex->H % 256 != 0) return MOE_EUNSUPPORTED;
+  if (tiled8 && (!a4(ex->s1) || !a4(ex->s3) || !a4(ex->s2))) return MOE_EINVAL;
   if (ex->has_shared) {
     if (!ex->sw1 || !ex->sw3 || !ex->sw2) return MOE_EINVAL;
     if (!aligned16(ex->sw1) || !aligned16(ex->sw3) || !aligned16(ex->sw2)) return MOE_EINVAL;
     if (scaled && (!ex->ss1 || !ex->ss3 || !ex->ss2)) return MOE_EINVAL;
-    if (ex->wtype == MOE_W_MXFP8 && (!a4(ex->ss1) || !a4(ex->ss3) || !a4(ex->ss2))) return MOE_EINVAL;
+    if (tiled8 && (!a4(ex->ss1) || !a4(ex->ss3) || !a4(ex->ss2))) return MOE_EINVAL;
   }
   return MOE_OK;
 }
@@ -84,8 +88,9 @@ GemmArgs gemm_args(const moe_experts_t* ex, int64_t T, int k, const int32_t* off
   GemmArgs a;
   a.w1 = ex->w1; a.w3 = ex->w3; a.w2 = ex->w2;
   a.sw1 = ex->sw1; a.sw3 = ex->sw3; a.sw2 = ex->sw2;
-  // fp32 128x128 block scales (MOE_W_FP8) or E8M0 bytes (MOE_W_MXFP8); each
-  // kernel family reads them in its own format
+  // fp32 128x128 block scales (MOE_W_FP8), E8M0 bytes (MOE_W_MXFP8) or one
+  // fp32 per matrix (MOE_W_FP8_TENSOR); each kernel family reads them in its
+  // own format
   a.s1 = static_cast<const float*>(ex->s1); a.s3 = static_cast<const float*>(ex->s3);
   a.s2 = static_cast<const float*>(ex->s2);
   a.ss1 = static_cast<const float*>(ex->ss1); a.ss3 = static_cast<const float*>(ex->ss3);
@@ -234,6 +239,45 @@ int moe_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, ui
   MOE_GUARD_END
 }
 
+namespace {
+int check_tensors(const void* x, int dtype, int64_t mats, int64_t n) {
+  if (mats < 0 || n < 0) return MOE_EINVAL;
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_EUNSUPPORTED;
+  if (n % 128 != 0 || mats > 65535 || mats * n >= (int64_t)1 << 40) return MOE_EUNSUPPORTED;
+  if (mats == 0 || n == 0) return MOE_OK;
+  if (!x || !aligned16(x)) return MOE_EINVAL;
+  return MOE_OK;
+}
+size_t elem_bytes(int dtype) { return dtype == MOE_DTYPE_F32 ? 4 : 2; }
+}  // namespace
+
+int moe_tensor_amax(const void* x, int dtype, int64_t mats, int64_t n, float* amax, void* stream) {
+  MOE_GUARD_BEGIN
+  const int st = check_tensors(x, dtype, mats, n);
+  if (st != MOE_OK || mats == 0 || n == 0) return st;
+  if (!amax || (reinterpret_cast<uintptr_t>(amax) & 3u)) return MOE_EINVAL;
+  if (overlap(amax, (size_t)mats * 4, x, (size_t)(mats * n) * elem_bytes(dtype))) return MOE_EINVAL;
+  return device_status(launch_tensor_amax(x, dtype == MOE_DTYPE_F32, mats, n, amax, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
+int moe_quant_tensor_fp8(const void* x, int dtype, int64_t mats, int64_t n, const float* amax, uint8_t* q, float* s,
+                         void* stream) {
+  MOE_GUARD_BEGIN
+  const int st = check_tensors(x, dtype, mats, n);
+  if (st != MOE_OK || mats == 0 || n == 0) return st;
+  if (!amax || !q || !s) return MOE_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q) & 7u) || (reinterpret_cast<uintptr_t>(s) & 3u) ||
+      (reinterpret_cast<uintptr_t>(amax) & 3u))
+    return MOE_EINVAL;
+  const size_t xb = (size_t)(mats * n) * elem_bytes(dtype), qb = (size_t)(mats * n), sb = (size_t)mats * 4;
+  if (overlap(q, qb, x, xb) || overlap(s, sb, x, xb) || overlap(s, sb, q, qb) || overlap(q, qb, amax, sb))
+    return MOE_EINVAL;
+  return device_status(
+      launch_quant_tensor(x, dtype == MOE_DTYPE_F32, mats, n, amax, q, s, (hipStream_t)stream));
+  MOE_GUARD_END
+}
+
 // ------------------------------------------------------------------ grouped GEMMs
 size_t moe_gemm_workspace_bytes(const moe_experts_t* ex, int64_t T, int k) {
   (void)ex;
@@ -254,12 +298,15 @@ int moe_gemm13(const moe_experts_t* ex, const void* x, const void* xs, const int
   if (!x || !offsets || !slot_pair || !h) return MOE_EINVAL;
   if (!aligned16(x) || !aligned16(h)) return MOE_EINVAL;
   const bool mx = ex->wtype == MOE_W_MXFP8;
-  const bool fp8 = ex->wtype == MOE_W_FP8 || mx;
+  const bool pt = ex->wtype == MOE_W_FP8_TENSOR;
+  const bool fp8 = ex->wtype == MOE_W_FP8 || mx || pt;
   if (fp8 && (!xs || !hs)) return MOE_EINVAL;
-  if (mx && (reinterpret_cast<uintptr_t>(xs) & 3u)) return MOE_EINVAL;   // 4-byte scale words
+  if ((mx || pt) && (reinterpret_cast<uintptr_t>(xs) & 3u)) return MOE_EINVAL;   // 4-byte scale words
+  if (pt && (reinterpret_cast<uintptr_t>(hs) & 3u)) return MOE_EINVAL;
   const int64_t R = T * k + ex->has_shared * T;
-  const size_t hbytes = (size_t)R * ex->I * (fp8 ? 1 : 2);
-  const size_t hsbytes = mx ? (size_t)R * (ex->I / 32) : (size_t)R * (ex->I / 128) * 4;
+  // per-tensor: h is the unquantised fp32 h (its scale needs the whole tensor)
+  const size_t hbytes = (size_t)R * ex->I * (pt ? 4 : fp8 ? 1 : 2);
+  const size_t hsbytes = pt ? 4 : mx ? (size_t)R * (ex->I / 32) : (size_t)R * (ex->I / 128) * 4;
   if (overlap(h, hbytes, x, (size_t)T * ex->H * (fp8 ? 1 : 2))) return MOE_EINVAL;
   if (fp8 && overlap(hs, hsbytes, h, hbytes)) return MOE_EINVAL;
   if (ws == nullptr || ws_bytes < kGemmWsBytes) return MOE_EWORKSPACE;
@@ -268,6 +315,9 @@ int moe_gemm13(const moe_experts_t* ex, const void* x, const void* xs, const int
     return MOE_EINVAL;
   const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
   hipStream_t s = (hipStream_t)stream;
+  if (pt)
+    return device_status(launch_gemm13_pt(a, static_cast<const uint8_t*>(x), static_cast<const float*>(xs),
+                                          static_cast<float*>(h), static_cast<float*>(hs), static_cast<int*>(ws), s));
   if (mx)
     return device_status(launch_gemm13_mx(a, static_cast<const uint8_t*>(x), static_cast<const uint8_t*>(xs),
                                           static_cast<uint8_t*>(h), static_cast<uint8_t*>(hs), static_cast<int*>(ws), s));
@@ -293,14 +343,18 @@ int moe_gemm2(const moe_experts_t* ex, const void* h, const void* hs, const int3
   if (!h || !offsets || !y) return MOE_EINVAL;
   if (!aligned16(h) || !aligned16(y)) return MOE_EINVAL;
   const bool mx = ex->wtype == MOE_W_MXFP8;
-  const bool fp8 = ex->wtype == MOE_W_FP8 || mx;
+  const bool pt = ex->wtype == MOE_W_FP8_TENSOR;
+  const bool fp8 = ex->wtype == MOE_W_FP8 || mx || pt;
   if (fp8 && !hs) return MOE_EINVAL;
-  if (mx && (reinterpret_cast<uintptr_t>(hs) & 3u)) return MOE_EINVAL;   // 4-byte scale words
+  if ((mx || pt) && (reinterpret_cast<uintptr_t>(hs) & 3u)) return MOE_EINVAL;   // 4-byte scale words
   const int64_t R = T * k + ex->has_shared * T;
   if (overlap(y, (size_t)R * ex->H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2), h, (size_t)R * ex->I * (fp8 ? 1 : 2)))
     return MOE_EINVAL;
   const GemmArgs a = gemm_args(ex, T, k, offsets, nullptr);
   hipStream_t s = (hipStream_t)stream;
+  if (pt)
+    return device_status(
+        launch_gemm2_pt(a, static_cast<const uint8_t*>(h), static_cast<const float*>(hs), y, y_dtype, s));
   if (mx)
     return device_status(launch_gemm2_mx(a, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(hs), y,
                                          y_dtype, s));
@@ -362,14 +416,15 @@ int moe_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, co
 namespace {
 
 struct FwdLayout {
-  size_t ctl, logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, gemm_ws, xq, xs, h, hs, y, total;
+  size_t ctl, logits, ids, w, counts, offsets, slot_pair, pair_slot, align_ws, gemm_ws, xq, xs, h, hq, hs, y, total;
 };
 
 FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype, bool router) {
   FwdLayout L;
   const int64_t P = T * k, R = P + ex->has_shared * T;
   const bool mx = ex->wtype == MOE_W_MXFP8;
-  const bool fp8 = ex->wtype == MOE_W_FP8 || mx;
+  const bool pt = ex->wtype == MOE_W_FP8_TENSOR;
+  const bool fp8 = ex->wtype == MOE_W_FP8 || mx || pt;
   size_t off = 0;
   auto take = [&](size_t n) {
     const size_t at = off;
@@ -389,9 +444,11 @@ FwdLayout forward_layout(const moe_experts_t* ex, int64_t T, int k, int y_dtype,
   L.align_ws = take(moe_align_workspace_bytes(T, ex->E, k));
   L.gemm_ws = take(kGemmWsBytes);
   L.xq = take(fp8 ? (size_t)T * ex->H : 0);
-  L.xs = take(mx ? (size_t)T * (ex->H / 32) : fp8 ? (size_t)T * (ex->H / 128) * 4 : 0);
-  L.h = take((size_t)R * ex->I * (fp8 ? 1 : 2));
-  L.hs = take(mx ? (size_t)R * (ex->I / 32) : fp8 ? (size_t)R * (ex->I / 128) * 4 : 0);
+  // per-tensor: xs / hs hold {amax, scale}; h is fp32, the codes go to hq
+  L.xs = take(pt ? 8 : mx ? (size_t)T * (ex->H / 32) : fp8 ? (size_t)T * (ex->H / 128) * 4 : 0);
+  L.h = take((size_t)R * ex->I * (pt ? 4 : fp8 ? 1 : 2));
+  L.hq = take(pt ? (size_t)R * ex->I : 0);
+  L.hs = take(pt ? 8 : mx ? (size_t)R * (ex->I / 32) : fp8 ? (size_t)R * (ex->I / 128) * 4 : 0);
   L.y = take((size_t)R * ex->H * (y_dtype == MOE_DTYPE_F32 ? 4 : 2));
   L.total = off;
   return L;
@@ -457,6 +514,7 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   hipStream_t s = (hipStream_t)stream;
   const int E = ex->E;
   const bool mx = ex->wtype == MOE_W_MXFP8;
+  const bool pt = ex->wtype == MOE_W_FP8_TENSOR;
   const bool fp8 = ex->wtype == MOE_W_FP8;
   float* logits = router ? reinterpret_cast<float*>(base + L.logits) : nullptr;
   int32_t* ids = args->topk_ids ? args->topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
@@ -482,7 +540,23 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   e = launch_align(ids, T, E, k, ex->has_shared, counts, offsets, slot_pair, pair_slot, align_ws, s);
   if (e != hipSuccess) return MOE_EDEVICE;
   const GemmArgs a = gemm_args(ex, T, k, offsets, slot_pair);
-  if (mx) {
+  if (pt) {
+    // x: amax, then codes with one scale; Gate-Up: fp32 h and its amax; h:
+    // codes with one scale; Down
+    float* xsw = reinterpret_cast<float*>(base + L.xs);   // {amax, scale}
+    float* hsw = reinterpret_cast<float*>(base + L.hs);
+    uint8_t* hq = reinterpret_cast<uint8_t*>(base + L.hq);
+    const int64_t R = T * k + ex->has_shared * T;
+    e = launch_tensor_amax(args->x, 0, 1, T * ex->H, xsw, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_quant_tensor(args->x, 0, 1, T * ex->H, xsw, xq, xsw + 1, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm13_pt(a, xq, xsw + 1, static_cast<float*>(h), hsw, reinterpret_cast<int*>(base + L.gemm_ws), s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_quant_tensor(h, 1, 1, R * ex->I, hsw, hq, hsw + 1, s);
+    if (e != hipSuccess) return MOE_EDEVICE;
+    e = launch_gemm2_pt(a, hq, hsw + 1, y, args->y_dtype, s);
+  } else if (mx) {
     uint8_t* xsm = reinterpret_cast<uint8_t*>(base + L.xs);
     uint8_t* hsm = reinterpret_cast<uint8_t*>(base + L.hs);
     e = launch_quant_rows_mx(args->x, T, ex->H, xq, xsm, s);

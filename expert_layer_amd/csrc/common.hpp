@@ -91,6 +91,11 @@ hipError_t launch_quant_blocks(const uint16_t* w, int64_t mats, int rows, int co
                                float* sc, hipStream_t s);
 hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                                 hipStream_t s);
+// per-tensor FP8: amax[m] = max |x| of tensor m (mats tensors of n values,
+// bf16 or fp32 when f32), then s[m] = amax/448 (1 if 0) and q = e4m3(x / s[m])
+hipError_t launch_tensor_amax(const void* x, int f32, int64_t mats, int64_t n, float* amax, hipStream_t s);
+hipError_t launch_quant_tensor(const void* x, int f32, int64_t mats, int64_t n, const float* amax, uint8_t* q,
+                               float* sc, hipStream_t s);
 
 hipError_t launch_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, const float* w, int64_t T,
                                   int k, int H, int has_shared, const uint16_t* residual, const uint16_t* weight,
@@ -129,6 +134,12 @@ bool tiled_mx_gemm2_ok(const GemmArgs& a);
 hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
                             int* sync, hipStream_t s);
 hipError_t launch_gemm2_mx(const GemmArgs& a, const uint8_t* hq, const uint8_t* hs, void* y, int y_dtype,
+                           hipStream_t s);
+// per-tensor FP8 (same tiles): weight scales s1/s3/s2 [E] and ss1/ss3/ss2 [1]
+// fp32; xs, hs [1]; the Gate-Up writes fp32 h [R, I] and hamax = max |h|
+hipError_t launch_gemm13_pt(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
+                            int* sync, hipStream_t s);
+hipError_t launch_gemm2_pt(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
                            hipStream_t s);
 
 bool tiled_fp8_gemm13_ok(const GemmArgs& a);

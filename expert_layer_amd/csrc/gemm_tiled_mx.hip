@@ -21,6 +21,16 @@
 // the row amax is a 16-lane shuffle.  The Gate-Up workgroups of one XCD meet
 // at a counter in the caller's workspace after every round of items (bounded
 // wait; it only affects timing).
+//
+// PT = 1 is the per-tensor FP8 mode (HPC-Ops page, main functions: the
+// GroupGEMM supports per-tensor as well as block-wise FP8): the same tiles
+// and loads without the scale words, unit E8M0 scales for the matrix cores,
+// and the code products accumulated over the whole K are scaled once in the
+// epilogue by (activation tensor scale x the expert matrix's scale).  The
+// Gate-Up epilogue writes h in fp32 and keeps the running max of |h|; each
+// workgroup folds it into one word with an integer atomicMax (bit patterns of
+// non-negative floats order like their values, so the result does not depend
+// on the order of the updates), from which the per-tensor h scale follows.
 #include "tiles.hpp"
 
 namespace moe355 {
@@ -64,19 +74,23 @@ __device__ __forceinline__ i32x8_t read_frag(const i32x4_t* plo, const i32x4_t* 
   return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__global__ void clear_sync_mx(int* sync) {
+// sync: 8 round counters; word (may be NULL): the h amax of the per-tensor mode
+__global__ void clear_sync_mx(int* sync, unsigned* word) {
   if (threadIdx.x < 8) sync[threadIdx.x] = 0;
+  if (threadIdx.x == 8 && word != nullptr) *word = 0u;
 }
 
-template <int MODE, int YBF16>  // MODE 0: Gate-Up (+SwiGLU, MX-requantised h); MODE 1: Down (y)
+// MODE 0: Gate-Up (+SwiGLU; MX: requantised h, PT: fp32 h + amax); MODE 1: Down (y)
+template <int MODE, int YBF16, int PT = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const uint8_t* __restrict__ A,
                                                              const uint8_t* __restrict__ As,
                                                              void* __restrict__ out,
                                                              uint8_t* __restrict__ out_s,
                                                              int* __restrict__ sync) {
+  constexpr int kScaleRows = PT ? 1 : kTM;
   __shared__ __attribute__((aligned(1024))) i32x4_t a0[kTM * kSlots], a1[kTM * kSlots];
   __shared__ __attribute__((aligned(1024))) i32x4_t b0[kTN * kSlots], b1[kTN * kSlots];
-  __shared__ __attribute__((aligned(16))) int sa0[kTM], sa1[kTM], sb0[kTN], sb1[kTN];
+  __shared__ __attribute__((aligned(16))) int sa0[kScaleRows], sa1[kScaleRows], sb0[kScaleRows], sb1[kScaleRows];
   __shared__ ChunkTable tab;
 
   const int G = a.E + (a.has_shared ? 1 : 0);
@@ -105,6 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
   __shared__ int sync_on;
   if (threadIdx.x == 0) sync_on = (sync != nullptr && nblk % 8 == 0) ? 1 : 0;
   const int64_t rounds = (items + nblk - 1) / nblk;
+  float hmax = 0.0f;  // PT Gate-Up: running max |h| of this thread's outputs
   for (int64_t rnd = 0; rnd < rounds; ++rnd) {
    const int64_t it = worker + rnd * nblk;
    if (it < items) {
@@ -165,8 +180,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
     }
     // scale words: waves 0-3 load the A rows 64*wave + lane, waves 4-7 the
     // weight rows 64*(wave-4) + lane of the tile (KM bytes per row in memory)
-    const uint8_t* ssrc;
-    if (wave < 4) {
+    const uint8_t* ssrc = nullptr;
+    if (PT) {
+    } else if (wave < 4) {
       const int row = 64 * wave + lane;
       const int r = r0 + min(row, nrows - 1);
       const int64_t srow = MODE == 0 ? (r < P ? (int64_t)(a.slot_pair[r] / a.k) : (int64_t)r - P) : (int64_t)r;
@@ -192,10 +208,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
         load_lds16(A + a_off[i] + k0, &la[(4 * wave + i) * 64]);
         load_lds16(bw + b_off[i] + k0, &lb[(4 * wave + i) * 64]);
       }
-      if (wave < 4)
+      if (PT) {
+      } else if (wave < 4) {
         load_lds4(ssrc + 4 * kb, &lsa[64 * wave]);
-      else
+      } else {
         load_lds4(ssrc + 4 * kb, &lsb[64 * (wave - 4)]);
+      }
     };
 
     f32x4_t acc[8][4];
@@ -214,21 +232,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
       const i32x4_t* ahi = la + 128 * wm * kSlots + off_hi;
       const i32x4_t* blo = lb + brow0 * kSlots + off_lo;
       const i32x4_t* bhi = lb + brow0 * kSlots + off_hi;
-      const int* psa = lsa + 128 * wm + lr;
-      const int* psb = lsb + brow0 + lr;
+      const int* psa = lsa + (PT ? 0 : 128 * wm + lr);
+      const int* psb = lsb + (PT ? 0 : brow0 + lr);
       i32x8_t bfr[4];
       int sb[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
         bfr[f] = read_frag(blo, bhi, fr);
-        sb[f] = psb[fr] >> bsh;   // byte 0 = this lane's block scale (upper bytes ignored)
+        sb[f] = PT ? 127 : psb[fr] >> bsh;   // byte 0 = this lane's block scale (upper bytes ignored)
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (m < mfw) {
           const i32x8_t af = read_frag(alo, ahi, 16 * m);
-          const int sa = psa[16 * m] >> bsh;
+          const int sa = PT ? 127 : psa[16 * m] >> bsh;
 #pragma unroll
           for (int f = 0; f < 4; ++f) acc[m][f] = mfma_mx(af, bfr[f], acc[m][f], sa, sb[f]);
         }
@@ -257,7 +275,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
     }
 
     // ---- epilogue
-    if (MODE == 0) {
+    if (MODE == 0 && PT) {
+      // h = SiLU(g) * u in fp32 with g = acc * (xs * s1[g]), u = acc * (xs * s3[g])
+      const float xsc = reinterpret_cast<const float*>(As)[0];
+      const float gs = xsc * (shared ? a.ss1[0] : a.s1[g]);
+      const float us = xsc * (shared ? a.ss3[0] : a.s3[g]);
+      float* hf = static_cast<float*>(out);
+      const int col = nt * (kTN / 2) + 32 * wn + lr;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m < mfw) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 128 * wm + 16 * m + 4 * lq + i;
+            if (row < nrows) {
+              const float h0 = silu_mul(acc[m][0][i] * gs, acc[m][2][i] * us);
+              const float h1 = silu_mul(acc[m][1][i] * gs, acc[m][3][i] * us);
+              const int64_t r = r0 + row;
+              hf[r * I + col] = h0;
+              hf[r * I + col + 16] = h1;
+              hmax = fmaxf(hmax, fmaxf(fabsf(h0), fabsf(h1)));
+            }
+          }
+        }
+      }
+    } else if (MODE == 0) {
       // h = SiLU(g) * u; this wave's 32 columns of a row are one MX block
       uint8_t* hq = static_cast<uint8_t*>(out);
       const int col = nt * (kTN / 2) + 32 * wn + lr;
@@ -281,6 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
         }
       }
     } else {
+      // PT: y = acc * (hs * s2[g]); MX: the scales are already applied
+      const float ysc = PT ? reinterpret_cast<const float*>(As)[0] * (shared ? a.ss2[0] : a.s2[g]) : 1.0f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (m < mfw) {
@@ -292,10 +336,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
               const int col = nt * kTN + 64 * wn + lr;
 #pragma unroll
               for (int f = 0; f < 4; ++f) {
+                const float v = PT ? acc[m][f][i] * ysc : acc[m][f][i];
                 if (YBF16)
-                  static_cast<uint16_t*>(out)[r * H + col + 16 * f] = (uint16_t)f32_to_bf16(acc[m][f][i]);
+                  static_cast<uint16_t*>(out)[r * H + col + 16 * f] = (uint16_t)f32_to_bf16(v);
                 else
-                  static_cast<float*>(out)[r * H + col + 16 * f] = acc[m][f][i];
+                  static_cast<float*>(out)[r * H + col + 16 * f] = v;
               }
             }
           }
@@ -321,6 +366,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
       __syncthreads();
     }
   }
+  if (MODE == 0 && PT) {
+    __shared__ float red[kThreads / 64];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+    if (lane == 0) red[wave] = hmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mx = red[0];
+      for (int w = 1; w < kThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+      if (mx > 0.0f) atomicMax(reinterpret_cast<unsigned*>(out_s), __float_as_uint(mx));
+    }
+  }
 }
 
 }  // namespace
@@ -331,8 +388,26 @@ bool tiled_mx_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
 
 hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
                             int* sync, hipStream_t s) {
-  clear_sync_mx<<<1, 64, 0, s>>>(sync);
+  clear_sync_mx<<<1, 64, 0, s>>>(sync, nullptr);
   gemm_tiled_mx<0, 0><<<device_cus(), kThreads, 0, s>>>(a, xq, xs, hq, hs, sync);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm13_pt(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
+                            int* sync, hipStream_t s) {
+  clear_sync_mx<<<1, 64, 0, s>>>(sync, reinterpret_cast<unsigned*>(hamax));
+  gemm_tiled_mx<0, 0, 1><<<device_cus(), kThreads, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
+                                                          reinterpret_cast<uint8_t*>(hamax), sync);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_pt(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
+                           hipStream_t s) {
+  const uint8_t* hsb = reinterpret_cast<const uint8_t*>(hs);
+  if (y_dtype == 1)
+    gemm_tiled_mx<1, 1, 1><<<device_cus(), kThreads, 0, s>>>(a, hq, hsb, y, nullptr, nullptr);
+  else
+    gemm_tiled_mx<1, 0, 1><<<device_cus(), kThreads, 0, s>>>(a, hq, hsb, y, nullptr, nullptr);
   return hipGetLastError();
 }
 

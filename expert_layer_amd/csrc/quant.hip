@@ -9,6 +9,12 @@
 //            beside the 128x128 scales): per row, per 32 columns, an E8M0
 //            byte X + 127 with X = floor(log2(amax)) - 8 and codes
 //            e4m3(v * 2^-X) (exact power-of-two scaling, then RNE/saturation).
+//  * tensor: one scale per tensor (the per-tensor FP8 mode of the HPC-Ops
+//            page's GroupGEMM, main functions), bf16 or fp32 values; the
+//            amax is a separate pass (max over every workgroup, combined
+//            with an integer atomicMax on the bit patterns of non-negative
+//            floats, which orders like the values and does not depend on the
+//            order of the updates).
 #include "common.hpp"
 
 namespace moe355 {
@@ -129,7 +135,109 @@ __global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t* __re
   }
 }
 
+// 8 consecutive values of a bf16 (F32 = 0) or fp32 (F32 = 1) array at i
+template <int F32>
+__device__ __forceinline__ void load8(const void* x, int64_t i, float v[8]) {
+  if (F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + i);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + i);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+  }
+}
+
+template <int F32>
+__device__ __forceinline__ const void* tensor_base(const void* x, int64_t m, int64_t n) {
+  return F32 ? static_cast<const void*>(static_cast<const float*>(x) + m * n)
+             : static_cast<const void*>(static_cast<const uint16_t*>(x) + m * n);
+}
+
+__global__ void zero_words(unsigned* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// amax[m] |= max |x| over tensor m (blockIdx.y); amax starts at 0
+template <int F32>
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, int64_t n,
+                                                          unsigned* __restrict__ amax) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.y;
+  const void* base = tensor_base<F32>(x, m, n);
+  float mx = 0.0f;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+    float v[8];
+    load8<F32>(base, i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (mx > 0.0f) atomicMax(amax + m, __float_as_uint(mx));
+  }
+}
+
+// s[m] = amax[m] / 448 (1 if 0), q = e4m3(fp32(x / s[m])) over tensor m (blockIdx.y)
+template <int F32>
+__global__ __launch_bounds__(256) void quant_tensor_kernel(const void* __restrict__ x, int64_t n,
+                                                           const float* __restrict__ amax,
+                                                           uint8_t* __restrict__ q, float* __restrict__ sc) {
+  const int64_t m = blockIdx.y;
+  const float a = amax[m];
+  const float s = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) sc[m] = s;
+  const void* base = tensor_base<F32>(x, m, n);
+  uint8_t* qm = q + m * n;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+    float v[8];
+    load8<F32>(base, i, v);
+    const uint32_t lo = f32x2_to_e4m3(__fdiv_rn(v[0], s), __fdiv_rn(v[1], s)) |
+                        (f32x2_to_e4m3(__fdiv_rn(v[2], s), __fdiv_rn(v[3], s)) << 16);
+    const uint32_t hi = f32x2_to_e4m3(__fdiv_rn(v[4], s), __fdiv_rn(v[5], s)) |
+                        (f32x2_to_e4m3(__fdiv_rn(v[6], s), __fdiv_rn(v[7], s)) << 16);
+    *reinterpret_cast<uint2*>(qm + i) = make_uint2(lo, hi);
+  }
+}
+
+dim3 tensor_grid(int64_t mats, int64_t n) {
+  const int64_t per = std::min<int64_t>((n + 2047) / 2048, std::max<int64_t>(1, 2048 / std::max<int64_t>(1, mats)));
+  return dim3((unsigned)std::max<int64_t>(1, per), (unsigned)mats);
+}
+
 }  // namespace
+
+hipError_t launch_tensor_amax(const void* x, int f32, int64_t mats, int64_t n, float* amax, hipStream_t s) {
+  unsigned* a = reinterpret_cast<unsigned*>(amax);
+  zero_words<<<(unsigned)std::min<int64_t>((mats + 255) / 256, 64), 256, 0, s>>>(a, mats);
+  const dim3 grid = tensor_grid(mats, n);
+  if (f32)
+    tensor_amax_kernel<1><<<grid, 256, 0, s>>>(x, n, a);
+  else
+    tensor_amax_kernel<0><<<grid, 256, 0, s>>>(x, n, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor(const void* x, int f32, int64_t mats, int64_t n, const float* amax, uint8_t* q,
+                               float* sc, hipStream_t s) {
+  const dim3 grid = tensor_grid(mats, n);
+  if (f32)
+    quant_tensor_kernel<1><<<grid, 256, 0, s>>>(x, n, amax, q, sc);
+  else
+    quant_tensor_kernel<0><<<grid, 256, 0, s>>>(x, n, amax, q, sc);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows_mx(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                                 hipStream_t s) {

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE355_ABI_VERSION 3
+#define MOE355_ABI_VERSION 4
 
 enum {
   MOE_OK = 0,
@@ -56,7 +56,7 @@ enum {
 };
 
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };  /* y_dtype */
-enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_MXFP8 = 2 };   /* moe_experts_t.wtype */
+enum { MOE_W_BF16 = 0, MOE_W_FP8 = 1, MOE_W_MXFP8 = 2, MOE_W_FP8_TENSOR = 3 };   /* moe_experts_t.wtype */
 
 int moe_abi_version(void);
 const char* moe_status_string(int status);
@@ -139,6 +139,26 @@ int moe_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, ui
  */
 int moe_quant_rows_mxfp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, uint8_t* s, void* stream);
 
+/* ------------------------------------------------------------------ per-tensor FP8 helpers
+ * The per-tensor FP8 mode of the HPC-Ops page's GroupGEMM (main functions:
+ * per-tensor as well as block-wise FP8): one fp32 scale per tensor.  x holds
+ * mats tensors of n values each (dtype MOE_DTYPE_BF16 or MOE_DTYPE_F32).
+ * moe_tensor_amax: amax[m] = max |x| over tensor m (fp32).  The call zeroes
+ *   amax first; the result does not depend on the order of the partial
+ *   maxima.
+ * moe_quant_tensor_fp8: s[m] = amax[m] / 448 in fp32 (1 when amax[m] == 0),
+ *   q = e4m3(fp32(v / s[m])) (round to nearest even, saturating), from an amax
+ *   computed by moe_tensor_amax or by the per-tensor Gate-Up GEMM.
+ * Used offline for expert weights (w1, w3, w2 as E tensors of I*H values, the
+ * shared ones as 1), on the hot path for x (1 tensor of T*H values) and for
+ * h (1 tensor of R*I fp32 values).  n must be a multiple of 128 and
+ * mats <= 65535 (MOE_EUNSUPPORTED); x 16-byte, q 8-byte, amax and s 4-byte
+ * aligned; q and s must overlap neither x nor each other (MOE_EINVAL).
+ */
+int moe_tensor_amax(const void* x, int dtype, int64_t mats, int64_t n, float* amax, void* stream);
+int moe_quant_tensor_fp8(const void* x, int dtype, int64_t mats, int64_t n, const float* amax, uint8_t* q, float* s,
+                         void* stream);
+
 /* ------------------------------------------------------------------ experts
  * SwiGLU experts: h = SiLU(x.w1^T) * (x.w3^T) (w1 = gate, w3 = up),
  * y = h.w2^T.  Routed: w1, w3 [E,I,H], w2 [E,H,I].  Shared expert (if
@@ -147,15 +167,18 @@ int moe_quant_rows_mxfp8(const uint16_t* x, int64_t rows, int cols, uint8_t* q, 
  * scales s1, s3 [E,I/128,H/128], s2 [E,H/128,I/128], ss1, ss3 [I/128,H/128],
  * ss2 [H/128,I/128].  wtype MOE_W_MXFP8: e4m3 codes plus uint8 E8M0 scales per
  * weight row per 32 K (moe_quant_rows_mxfp8): s1, s3 [E,I,H/32], s2
- * [E,H,I/32], ss1, ss3 [I,H/32], ss2 [H,I/32], 4-byte aligned (MOE_EINVAL
- * otherwise); H must be a multiple of 256 (MOE_EUNSUPPORTED otherwise).  The struct itself is host memory; the
- * pointers in it are device pointers.
+ * [E,H,I/32], ss1, ss3 [I,H/32], ss2 [H,I/32].  wtype MOE_W_FP8_TENSOR: e4m3
+ * codes plus one fp32 scale per matrix (moe_quant_tensor_fp8): s1, s3, s2 [E],
+ * ss1, ss3, ss2 [1].  MXFP8 and per-tensor scale pointers must be 4-byte
+ * aligned (MOE_EINVAL otherwise) and H a multiple of 256 (MOE_EUNSUPPORTED
+ * otherwise).  The struct itself is host memory; the pointers in it are
+ * device pointers.
  */
 typedef struct moe_experts_t {
   int wtype;
   int E, H, I, has_shared;
   const void *w1, *w3, *w2;
-  const void *s1, *s3, *s2;     /* fp32 (MOE_W_FP8) or uint8 E8M0 (MOE_W_MXFP8) */
+  const void *s1, *s3, *s2;     /* fp32 (MOE_W_FP8, MOE_W_FP8_TENSOR) or uint8 E8M0 (MOE_W_MXFP8) */
   const void *sw1, *sw3, *sw2;
   const void *ss1, *ss3, *ss2;
 } moe_experts_t;
@@ -176,6 +199,13 @@ typedef struct moe_experts_t {
  *   aligned); the matrix cores apply the E8M0 scales of both operands per 32 K;
  *   h is requantised per row per 32 columns with the same rule as
  *   moe_quant_rows_mxfp8 into h e4m3 [R,I] and hs uint8 [R,I/32].
+ * per-tensor fp8: x e4m3 [T,H] with xs fp32 [1] (moe_quant_tensor_fp8 of the
+ *   whole x); the code products summed over the whole K are scaled by
+ *   xs[0] * s1[g] (s3[g] for the up half).  A per-tensor scale needs the amax
+ *   of the whole h before any code, so this stage writes h unquantised, fp32
+ *   [R,I], and hs fp32 [1] receives max |h|; moe_quant_tensor_fp8(h,
+ *   MOE_DTYPE_F32, 1, R*I, hs, ...) then gives the codes and scale that
+ *   moe_gemm2 takes.  xs and hs 4-byte aligned.
  * offsets, slot_pair: from moe_align.
  * ws: device scratch of moe_gemm_workspace_bytes bytes, 4-byte aligned; its
  *   contents need not be initialised (the call clears what it uses, on its
@@ -195,7 +225,9 @@ int moe_gemm13(const moe_experts_t* ex, const void* x, const void* xs, const int
 /* ------------------------------------------------------------------ stage 4: Down GEMM
  * y[s] = h[s].w2[g]^T for every slot s of group g (fp32 accumulation; fp8
  * partial sums per 128-wide K block scaled by hs[s,kb] * s2[g,n/128,kb];
- * mxfp8: hs uint8 [R,I/32], 4-byte aligned, scales applied per 32 K).
+ * mxfp8: hs uint8 [R,I/32], 4-byte aligned, scales applied per 32 K;
+ * per-tensor fp8: h e4m3 [R,I], hs fp32 [1], sums over the whole K scaled by
+ * hs[0] * s2[g]).
  * y is fp32 (y_dtype MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16), [R,H].
  * ws, ws_bytes: reserved, unused (NULL and 0 are accepted).
  */
@@ -229,7 +261,8 @@ int moe_combine_rmsnorm(const void* y, int y_dtype, const int32_t* pair_slot, co
 
 /* ------------------------------------------------------------------ the whole chain
  * Convenience entry point that enqueues the chain on one stream:
- * [router_gemm] -> route -> align -> [quant_rows_fp8] -> gemm13 -> gemm2 -> combine.
+ * [router_gemm] -> route -> align -> [quant x] -> gemm13 -> [quant h] -> gemm2 -> combine
+ * (x and, for per-tensor FP8, h quantised as the weight type prescribes).
  * Either logits (fp32 [T,E]) or the split router weights (router_hi/lo bf16
  * [E,H]) must be given.  x bf16 [T,H]; out bf16 [T,H].  Every intermediate
  * lives in the caller's workspace (moe_forward_workspace_bytes bytes); the

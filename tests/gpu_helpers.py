@@ -20,7 +20,7 @@ import workloads
 from expert_layer_amd.chain import Buffers, Layer, run_chain, split_router
 from oracle import oracle as orc
 
-TOL = {"bf16": 1e-2, "fp8": 5e-2, "mxfp8": 5e-2}
+TOL = {"bf16": 1e-2, "fp8": 5e-2, "mxfp8": 5e-2, "fp8t": 5e-2}
 
 
 def log(msg):
@@ -35,7 +35,7 @@ def host(t):
 def run_gpu(wl, d, y_dtype=torch.float32):
     fp8 = wl.wtype == "fp8"
     layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=fp8,
-                               mx=wl.wtype == "mxfp8")
+                               mx=wl.wtype == "mxfp8", pt=wl.wtype == "fp8t")
     b = Buffers(layer, wl.T, wl.k, y_dtype=y_dtype, router=wl.router)
     hi = lo = None
     if wl.router:
@@ -133,6 +133,49 @@ def check_layer(wl, d, y_dtype=torch.float32, check_rows=None):
                       s1=qs["w1"][1], s3=qs["w3"][1], s2=qs["w2"][1],
                       ss1=sq["sw1"][1] if wl.shared else None, ss3=sq["sw3"][1] if wl.shared else None,
                       ss2=sq["sw2"][1] if wl.shared else None)
+        ids_c = ids_ref.copy()
+        ids_c[rows] = remap[ids_ref[rows]]
+        ref = orc.layer_rows(L, xq_ref, ids_c, w_ref, rows, xs=xs_ref)
+    elif wl.wtype == "fp8t":
+        # x: one scale; codes bit-exact
+        xv = (x.astype(np.uint32) << 16).view(np.float32)   # the bf16 values, exactly
+        assert float(host(b.x_amax)[0]) == float(np.abs(xv).max()), "x amax"
+        xq_ref, xs_ref = orc.quant_tensor_fp8(x)
+        assert np.array_equal(host(b.xq), xq_ref), "x codes"
+        assert np.array_equal(host(b.xs), xs_ref), "x scale"
+        # weights of the experts the checked rows use: one scale per matrix
+        used = np.unique(ids_ref[rows].ravel())
+        uidx = torch.from_numpy(used).to(d["w1"].device)
+        ex = layer.experts.tensors
+        qs = {}
+        for name in ("w1", "w3", "w2"):
+            q, s_ = orc.quant_tensor_fp8(host(d[name][uidx]), mats=used.size)
+            assert np.array_equal(host(ex[name][uidx]), q), f"{name} codes"
+            assert np.array_equal(host(ex["s" + name[1:]][uidx]), s_), f"{name} scales"
+            qs[name] = (q, s_)
+        sq = {}
+        if wl.shared:
+            for name in ("sw1", "sw3", "sw2"):
+                q, s_ = orc.quant_tensor_fp8(host(d[name]))
+                assert np.array_equal(host(ex[name]), q), f"{name} codes"
+                assert np.array_equal(host(ex["ss" + name[2:]]), s_), f"{name} scales"
+                sq[name] = (q, s_)
+        # h: the GPU's fp32 h; its amax and codes must be exactly the max and
+        # the per-tensor quantisation of those values
+        hg = host(b.h)
+        assert float(host(b.h_amax)[0]) == float(np.abs(hg).max()), "h amax"
+        hq_ref, hs_ref = orc.quant_tensor_fp8(hg)
+        assert np.array_equal(host(b.hq), hq_ref), "h codes"
+        assert np.array_equal(host(b.hs), hs_ref), "h scale"
+        del hg
+        remap = np.full(E, -1, np.int32)
+        remap[used] = np.arange(used.size, dtype=np.int32)
+        gs = lambda n, i: sq[n][i] if wl.shared else None   # noqa: E731
+        # every row checked: the oracle's own h scale; a sample: the GPU's
+        h_scale = None if rows.size == wl.T else float(host(b.hs)[0])
+        L = orc.Layer(qs["w1"][0], qs["w3"][0], qs["w2"][0], gs("sw1", 0), gs("sw3", 0), gs("sw2", 0), wtype=3,
+                      s1=qs["w1"][1], s3=qs["w3"][1], s2=qs["w2"][1],
+                      ss1=gs("sw1", 1), ss3=gs("sw3", 1), ss2=gs("sw2", 1), h_scale=h_scale)
         ids_c = ids_ref.copy()
         ids_c[rows] = remap[ids_ref[rows]]
         ref = orc.layer_rows(L, xq_ref, ids_c, w_ref, rows, xs=xs_ref)

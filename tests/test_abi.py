@@ -34,14 +34,14 @@ def L():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     assert sorted(moe.exported_symbols()) == names
 
 
 def test_version_and_status_strings(L):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert moe.moe_status_string(0) == "ok"
     for s in range(1, 5):
         assert moe.moe_status_string(s) not in ("ok", "unknown status")
@@ -208,6 +208,35 @@ def test_forward_persistent_validation(L):
     args0 = moe.moe_forward_args_t(0, 2, 0, None, B, None, None, None, None, None, None, None)
     assert fp(ctypes.byref(ex), ctypes.byref(args0), None, 0, None) == moe.MOE_OK
     assert L.moe_forward_persistent_status(None, None) == moe.MOE_EINVAL
+
+
+def test_per_tensor_validation(L):
+    """Per-tensor FP8: the quantiser entry points and weight type 3 refuse bad
+    arguments before launching anything."""
+    amax = L.moe_tensor_amax
+    qt = L.moe_quant_tensor_fp8
+    F32, BF16 = moe.MOE_DTYPE_F32, moe.MOE_DTYPE_BF16
+    assert amax(A, 7, 1, 256, B, None) == moe.MOE_EUNSUPPORTED              # unknown dtype
+    assert amax(A, BF16, 1, 200, B, None) == moe.MOE_EUNSUPPORTED           # n % 128
+    assert amax(A, BF16, 70000, 128, B, None) == moe.MOE_EUNSUPPORTED       # too many tensors
+    assert amax(A, BF16, -1, 128, B, None) == moe.MOE_EINVAL
+    assert amax(A, BF16, 1, 256, None, None) == moe.MOE_EINVAL
+    assert amax(A + 2, BF16, 1, 256, B, None) == moe.MOE_EINVAL             # x not 16-byte aligned
+    assert amax(A, F32, 1, 256, A + 16, None) == moe.MOE_EINVAL             # amax inside x
+    assert amax(A, BF16, 0, 256, B, None) == moe.MOE_OK                     # nothing to do
+    assert qt(A, BF16, 1, 256, B, A + 64, D, None) == moe.MOE_EINVAL        # codes overlap x
+    assert qt(A, BF16, 1, 256, B, C, C + 8, None) == moe.MOE_EINVAL         # scale inside the codes
+    assert qt(A, BF16, 1, 256, B, C + 4, D, None) == moe.MOE_EINVAL         # codes not 8-byte aligned
+    assert qt(A, BF16, 1, 256, None, C, D, None) == moe.MOE_EINVAL
+    assert qt(A, BF16, 1, 0, B, C, D, None) == moe.MOE_OK
+    g13 = L.moe_gemm13
+    x, off, sp, h = 0x20000000, 0x21000000, 0x22000000, 0x23000000
+    pt = lambda **kw: _experts(wtype=3, H=256, s1=D, s3=D, s2=D, **kw)   # noqa: E731
+    assert g13(ctypes.byref(_experts(wtype=3, H=256)), x, B, off, sp, 4, 2, h, C, None, 0, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(pt(I=128)), x, B + 2, off, sp, 4, 2, h, C, 0x30000000, 256, None) == moe.MOE_EINVAL
+    assert g13(ctypes.byref(_experts(wtype=3, H=128, s1=D, s3=D, s2=D)), x, B, off, sp, 4, 2, h, C, 0x30000000,
+               256, None) == moe.MOE_EUNSUPPORTED                                # H % 256 for the Down tiles
+    assert g13(ctypes.byref(pt()), x, None, off, sp, 4, 2, h, C, 0x30000000, 256, None) == moe.MOE_EINVAL
 
 
 def test_router_validation(L):

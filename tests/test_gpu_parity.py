@@ -113,6 +113,62 @@ def test_mxfp8_quantiser_exhaustive_over_bf16():
         assert bad == 0, f"{bad} codes differ"
 
 
+PT_SMALL = [
+    W("pt-medium", T=300, H=512, E=16, k=4, I=256, shared=1, wtype="fp8t", seed=34),
+    W("pt-ragged", T=37, H=256, E=8, k=3, I=384, shared=0, wtype="fp8t", seed=35),
+    W("pt-zipf", T=400, H=256, E=32, k=8, I=256, shared=1, wtype="fp8t", bias="all", seed=36),
+    W("pt-tiny-groups", T=16, H=512, E=64, k=8, I=256, shared=1, wtype="fp8t", seed=37),
+]
+
+
+@pytest.mark.parametrize("wl", PT_SMALL, ids=[w.name for w in PT_SMALL])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16], ids=["yf32", "ybf16"])
+def test_small_fp8_per_tensor(wl, ydt):
+    check_layer(wl, _inputs(wl), y_dtype=ydt)
+
+
+def test_per_tensor_quantiser_over_bf16_and_f32():
+    """Every finite bf16 value through the GPU per-tensor amax + quantiser, as
+    256-value tensors (one scale each) as given and scaled across the exponent
+    range, and the same for fp32 tensors: amax, scales and codes equal the
+    oracle's bit for bit."""
+    import expert_layer_amd as moe
+    from oracle import oracle as orc
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    expo = (allbits >> 7) & 0xFF
+    finite = allbits[expo != 0xFF]
+    n = finite.size - finite.size % 256
+    rng = np.random.default_rng(10)
+    rows = rng.permutation(finite[:n]).reshape(-1, 256)
+    rows = np.concatenate([rows, np.arange(1, 257, dtype=np.uint16)[None], np.zeros((1, 256), np.uint16)])
+    vals = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).float().numpy()
+    with np.errstate(over="ignore"):
+        scaled = vals * np.ldexp(1.0, rng.integers(-40, 40, size=(vals.shape[0], 1))).astype(np.float32)
+    scaled = np.where(np.abs(scaled) < 3.0e38, scaled, 0.0).astype(np.float32)
+    scaled_bits = torch.from_numpy(scaled).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    f32 = np.where(np.abs(scaled) < 1e30, scaled * rng.standard_normal(scaled.shape).astype(np.float32), 0.0)
+    f32 = f32.astype(np.float32)
+    for data in (rows, scaled_bits, f32):
+        mats = data.shape[0]
+        if data.dtype == np.float32:
+            xg = torch.from_numpy(data).cuda()
+            amax_ref = np.abs(data).max(axis=1)
+        else:
+            xg = torch.from_numpy(data.view(np.int16)).view(torch.bfloat16).cuda()
+            amax_ref = np.abs((data.astype(np.uint32) << 16).view(np.float32)).max(axis=1)
+        amax = torch.empty(mats, dtype=torch.float32, device="cuda")
+        q = torch.empty(data.shape, dtype=torch.uint8, device="cuda")
+        s = torch.empty(mats, dtype=torch.float32, device="cuda")
+        moe.moe_tensor_amax(xg, amax, mats=mats)
+        moe.moe_quant_tensor_fp8(xg, amax, q, s, mats=mats)
+        torch.cuda.synchronize()
+        assert np.array_equal(amax.cpu().numpy(), amax_ref.astype(np.float32)), "amax differs"
+        rq, rs = orc.quant_tensor_fp8(data, mats=mats)
+        assert np.array_equal(s.cpu().numpy(), rs), "scales differ"
+        bad = np.sum(q.cpu().numpy() != rq)
+        assert bad == 0, f"{bad} codes differ"
+
+
 def test_forced_ties_and_one_hot():
     """Integer logits (many exact ties) and a batch where every token picks expert 5 first."""
     wl = W("ties", T=128, H=256, E=16, k=4, I=128, shared=1, seed=30)
@@ -213,7 +269,8 @@ def test_fp8_codec_exhaustive_over_bf16():
 # ---------------------------------------------------------------- the five layer configurations
 @pytest.mark.parametrize("name,ydt", [("tiny", torch.float32), ("decode", torch.float32),
                                       ("prefill", torch.bfloat16), ("fp8", torch.float32),
-                                      ("mxfp8", torch.float32), ("router", torch.bfloat16)])
+                                      ("mxfp8", torch.float32), ("fp8t", torch.float32),
+                                      ("router", torch.bfloat16)])
 def test_layer_configs(name, ydt):
     wl = workloads.WORKLOADS[name]
     d = _inputs(wl)

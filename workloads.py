@@ -12,6 +12,8 @@ Workloads (shapes and distributions of the five layer configurations):
            (128x128 block scales), Zipf-skewed routing
   mxfp8    the fp8 shape and routing with MXFP8 weights and activations
            (E8M0 scales per 32 values along K)
+  fp8t     the fp8 shape and routing with per-tensor FP8 (one scale per
+           expert matrix, per x, per h)
   router   T=16384 H=6144 E=256 k=8 I=2048 + shared expert, bf16, fp32 router
            weights [E,H], 30% of tokens carry the Zipf logit bias
 Distributions: weights bf16 ~N(0, 0.02), activations bf16 ~N(0, 1), router
@@ -37,7 +39,7 @@ class Workload:
     k: int
     I: int
     shared: int
-    wtype: str = "bf16"          # "bf16", "fp8" (128x128 scales) or "mxfp8"
+    wtype: str = "bf16"          # "bf16", "fp8" (128x128 scales), "mxfp8" or "fp8t" (per tensor)
     bias: str = "none"           # "none", "all" (every row biased) or "mix"
     bias_frac: float = 0.0       # fraction of biased rows for "mix"
     router: bool = False         # logits come from the split-bf16 router GEMM
@@ -64,6 +66,8 @@ WORKLOADS = {
                     bias="all", seed=1004),
     "mxfp8": Workload("mxfp8", T=4096, H=6144, E=256, k=8, I=2048, shared=1, wtype="mxfp8",
                       bias="all", seed=1006),
+    "fp8t": Workload("fp8t", T=4096, H=6144, E=256, k=8, I=2048, shared=1, wtype="fp8t",
+                     bias="all", seed=1007),
     "router": Workload("router", T=16384, H=6144, E=256, k=8, I=2048, shared=1, bias="mix",
                        bias_frac=0.3, router=True, seed=1005),
 }
