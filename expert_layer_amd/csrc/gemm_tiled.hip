@@ -7,23 +7,23 @@
 // waves load and compute (no warp specialisation) and latency is hidden by a
 // multi-stage LDS ring instead.
 //
-// Tile: up to 256 rows of one group x 256 weight rows (Gate-Up: 128 gate +
+// Tile: up to 256 or 288 rows of one group x 256 weight rows (Gate-Up: 128 gate +
 // 128 up columns of h; Down: 256 columns of y), 64 k per stage, so every row
 // of a stage is one whole 128-byte line (one L2 request per line; measured
 // faster than a deeper ring of half-line stages), a ring of 2 stages in LDS
-// (128 KB, one workgroup per CU).  Stages are filled with the gfx950
+// (128 or 136 KB, one workgroup per CU).  Stages are filled with the gfx950
 // direct-to-LDS 16-byte loads: each load instruction writes 1 KB of LDS (8
 // rows x 128 B) and every lane picks the global address whose 16 bytes belong
 // at its LDS slot, which realises the XOR swizzle that keeps MFMA fragment
 // reads free of bank conflicts.
 //
 // Eight waves, two per SIMD, in a 2 (rows) x 4 (weight rows) grid: wave w
-// computes rows 128*(w/4) .. +127 against 64 weight rows (Gate-Up: gate
+// computes rows TM/2*(w/4) .. +TM/2-1 against 64 weight rows (Gate-Up: gate
 // columns 32*(w%4) .. +31 and the matching up columns).  Waves are dealt to
 // SIMDs round robin, so waves w and w+4 share a SIMD and a weight slice: a
 // tile of up to 128 rows still keeps every SIMD's matrix core busy, and
 // 16-row fragments past the tile's valid rows are skipped.  A group with r
-// rows is cut into full 256-row tiles and a remainder tile.
+// rows is cut into full TM-row tiles and a remainder tile.
 //
 // Items (m-tile, n-tile) are ordered group by group, n-tile by n-tile, with
 // the m-tiles of one (group, n-tile) adjacent; a persistent grid of one
@@ -42,7 +42,6 @@ namespace moe355 {
 
 namespace {
 
-constexpr int kTM = 256;      // max rows per tile
 constexpr int kTN = 256;      // weight rows per tile
 constexpr int kTK = 64;       // k per stage (one 128-byte line per row)
 constexpr int kStages = 2;    // LDS ring depth
@@ -73,13 +72,15 @@ struct TileTable {
   int wsum[16];
 };
 
-// Tile t of a group of `cnt` rows: full 256-row tiles, then the remainder
-// (fragments past the valid rows are skipped, so a short remainder costs
-// little matrix-core time; its weight tile is read again, from the L2 of the
-// XCD that runs the group's full tiles next to it).
+// Tile t of a group of `cnt` rows: full TM-row tiles, then the remainder
+// (fragments past the valid rows are skipped, and so are the A loads of
+// 8-row groups past them, so a short remainder costs little matrix-core time
+// and load bandwidth; its weight tile is read again, from the L2 of the XCD
+// that runs the group's full tiles next to it).
+template <int TM>
 __device__ __forceinline__ void tile_rows(int cnt, int t, int& start, int& rows) {
-  start = t * kTM;
-  rows = min(kTM, cnt - start);
+  start = t * TM;
+  rows = min(TM, cnt - start);
 }
 
 constexpr int kSyncSpins = 1 << 14;   // bounded round barrier: ~1 ms at most
@@ -88,17 +89,24 @@ __global__ void clear_sync(int* sync) {
   if (threadIdx.x < 8) sync[threadIdx.x] = 0;
 }
 
-template <int MODE, int YBF16>  // MODE 0: Gate-Up (+SwiGLU, h bf16); MODE 1: Down (y)
+// MODE 0: Gate-Up (+SwiGLU, h bf16); MODE 1: Down (y).  MF: 16-row fragments
+// per wave, so a tile holds TM = 32 * MF rows (8: 256, 9: 288).
+template <int MODE, int YBF16, int MF>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint16_t* __restrict__ A,
                                                           void* __restrict__ out, int* __restrict__ sync) {
+  constexpr int TM = 32 * MF;
+  constexpr int NQ = TM / 8;              // 8-row load groups of the A tile
+  constexpr int NA = (NQ + 7) / 8;        // A loads per wave and stage: groups wave, wave + 8, ...
+  constexpr int HF = MF % 4 == 0 ? 4 : MF % 3 == 0 ? 3 : MF / 2;   // fragments per skip group
+  constexpr int NH = MF / HF;
   // one named array per ring stage: the stage being read and the stages being
   // filled are then provably distinct objects, so reads wait only for their own stage
-  __shared__ __attribute__((aligned(1024))) i32x4_t a0[kTM * kRowSlots], a1[kTM * kRowSlots];
+  __shared__ __attribute__((aligned(1024))) i32x4_t a0[TM * kRowSlots], a1[TM * kRowSlots];
   __shared__ __attribute__((aligned(1024))) i32x4_t b0[kTN * kRowSlots], b1[kTN * kRowSlots];
   __shared__ ChunkTable tab;
 
   const int G = a.E + (a.has_shared ? 1 : 0);
-  const int nmt_total = build_chunks(tab, a.offsets, G, kTM);
+  const int nmt_total = build_chunks(tab, a.offsets, G, TM);
   const int H = a.H, I = a.I;
   const int K = MODE == 0 ? H : I;            // reduction length
   const int NT = MODE == 0 ? (2 * I) / kTN : H / kTN;
@@ -139,16 +147,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
     const int nt = local / mtg, mt = local % mtg;
     const int cnt = a.offsets[g + 1] - a.offsets[g];
     int rs, nrows;
-    tile_rows(cnt, mt, rs, nrows);
+    tile_rows<TM>(cnt, mt, rs, nrows);
     const int r0 = a.offsets[g] + rs;
     const int nmf = (nrows + 15) >> 4;   // valid 16-row fragments
     const bool shared = g == a.E;
 
     // ---- per-lane global addresses for the direct-to-LDS loads (element offsets)
-    int a_off[4];
+    int a_off[NA];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 8 * (4 * wave + i) + lrow;
+    for (int i = 0; i < NA; ++i) {
+      const int row = 8 * min(wave + 8 * i, NQ - 1) + lrow;
       const int r = r0 + min(row, nrows - 1);
       int64_t base;
       if (MODE == 0) {
@@ -182,22 +190,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
       }
     }
 
+    // A loads of 8-row groups wholly past the valid rows are skipped (their
+    // LDS rows only feed accumulator rows that are never stored)
+    const int nq_live = min(NQ, (nrows + 7) / 8);
     auto issue = [&](int kk, i32x4_t* la, i32x4_t* lb) {
       const int k0 = kk * kTK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        load_lds16(A + a_off[i] + k0, &la[(4 * wave + i) * 64]);
-        load_lds16(bw + b_off[i] + k0, &lb[(4 * wave + i) * 64]);
-      }
+      for (int i = 0; i < NA; ++i)
+        if (wave + 8 * i < nq_live) load_lds16(A + a_off[i] + k0, &la[(wave + 8 * i) * 64]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_lds16(bw + b_off[i] + k0, &lb[(4 * wave + i) * 64]);
     };
 
-    f32x4_t acc[8][4];
+    f32x4_t acc[MF][4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < MF; ++m)
 #pragma unroll
       for (int f = 0; f < 4; ++f) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int mfw = min(8, max(0, nmf - 8 * wm));  // valid fragments of this wave
+    const int mfw = min(MF, max(0, nmf - MF * wm));  // valid fragments of this wave
 
     // fragments past the valid rows are skipped in halves of 4 (64 rows)
     // per-lane LDS bases: fragment f / m then sits at a compile-time offset
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
     auto compute = [&](const i32x4_t* la, const i32x4_t* lb) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const i32x4_t* pa = la + 128 * wm * kRowSlots + (j ? off1 : off0);
+        const i32x4_t* pa = la + 16 * MF * wm * kRowSlots + (j ? off1 : off0);
         const i32x4_t* pb = lb + brow0 * kRowSlots + (j ? off1 : off0);
         bf16x8_t bfr[4];
 #pragma unroll
@@ -216,15 +227,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
           bfr[f] = __builtin_bit_cast(bf16x8_t, pb[fr * kRowSlots]);
         }
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          if (mfw > 4 * hf) {
-            bf16x8_t af[4];
+        for (int hf = 0; hf < NH; ++hf) {
+          if (mfw > HF * hf) {
+            bf16x8_t af[HF];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) af[m] = __builtin_bit_cast(bf16x8_t, pa[16 * (4 * hf + m) * kRowSlots]);
+            for (int m = 0; m < HF; ++m) af[m] = __builtin_bit_cast(bf16x8_t, pa[16 * (HF * hf + m) * kRowSlots]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < HF; ++m)
 #pragma unroll
-              for (int f = 0; f < 4; ++f) acc[4 * hf + m][f] = mfma16(af[m], bfr[f], acc[4 * hf + m][f]);
+              for (int f = 0; f < 4; ++f) acc[HF * hf + m][f] = mfma16(af[m], bfr[f], acc[HF * hf + m][f]);
           }
         }
       }
@@ -259,11 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
 
     // ---- epilogue
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < MF; ++m) {
       if (m < mfw) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 128 * wm + 16 * m + 4 * lq + i;
+          const int row = 16 * MF * wm + 16 * m + 4 * lq + i;
           if (row < nrows) {
             const int64_t r = r0 + row;
             if (MODE == 0) {
@@ -313,17 +324,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
 bool tiled_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0; }
 bool tiled_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
 
+// Tile height: 288 rows when groups average 224 to 288 rows, so that a
+// typical group fits one tile and streams each weight tile once instead of
+// twice; else 256 (larger groups need two tiles at either height, and the
+// taller tile then only costs).
+static bool tall_tiles(const GemmArgs& a) {
+  const int64_t P = a.T * a.k;
+  return P > (int64_t)a.E * 224 && P <= (int64_t)a.E * 288;
+}
+
 hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s) {
   clear_sync<<<1, 64, 0, s>>>(sync);
-  gemm_tiled<0, 0><<<device_cus(), kThreads, 0, s>>>(a, x, h, sync);
+  if (tall_tiles(a))
+    gemm_tiled<0, 0, 9><<<device_cus(), kThreads, 0, s>>>(a, x, h, sync);
+  else
+    gemm_tiled<0, 0, 8><<<device_cus(), kThreads, 0, s>>>(a, x, h, sync);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_tiled(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s) {
-  if (y_dtype == 1)
-    gemm_tiled<1, 1><<<device_cus(), kThreads, 0, s>>>(a, h, y, nullptr);
-  else
-    gemm_tiled<1, 0><<<device_cus(), kThreads, 0, s>>>(a, h, y, nullptr);
+  const bool tall = tall_tiles(a);
+  if (y_dtype == 1) {
+    if (tall)
+      gemm_tiled<1, 1, 9><<<device_cus(), kThreads, 0, s>>>(a, h, y, nullptr);
+    else
+      gemm_tiled<1, 1, 8><<<device_cus(), kThreads, 0, s>>>(a, h, y, nullptr);
+  } else {
+    if (tall)
+      gemm_tiled<1, 0, 9><<<device_cus(), kThreads, 0, s>>>(a, h, y, nullptr);
+    else
+      gemm_tiled<1, 0, 8><<<device_cus(), kThreads, 0, s>>>(a, h, y, nullptr);
+  }
   return hipGetLastError();
 }
 

@@ -47,6 +47,9 @@ SMALL = [
     W("router-small", T=100, H=512, E=64, k=8, I=128, shared=1, router=True, bias="mix", bias_frac=0.3, seed=20),
     # router tiles of 128 tokens x 128 experts: ragged in both, two expert tiles
     W("router-ragged", T=300, H=384, E=200, k=8, I=128, shared=1, router=True, bias="mix", bias_frac=0.3, seed=21),
+    # 224 to 288 rows per expert on average: 288-row tiles, with remainders
+    # where the Zipf-biased experts overflow them
+    W("tall-tiles", T=500, H=256, E=16, k=8, I=128, shared=1, bias="mix", bias_frac=0.3, seed=38),
 ]
 
 
