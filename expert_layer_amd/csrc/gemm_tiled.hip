@@ -97,8 +97,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
   constexpr int TM = 32 * MF;
   constexpr int NQ = TM / 8;              // 8-row load groups of the A tile
   constexpr int NA = (NQ + 7) / 8;        // A loads per wave and stage: groups wave, wave + 8, ...
-  constexpr int HF = MF % 4 == 0 ? 4 : MF % 3 == 0 ? 3 : MF / 2;   // fragments per skip group
-  constexpr int NH = MF / HF;
   // one named array per ring stage: the stage being read and the stages being
   // filled are then provably distinct objects, so reads wait only for their own stage
   __shared__ __attribute__((aligned(1024))) i32x4_t a0[TM * kRowSlots], a1[TM * kRowSlots];
@@ -226,17 +224,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
           const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
           bfr[f] = __builtin_bit_cast(bf16x8_t, pb[fr * kRowSlots]);
         }
+        // A fragments in pairs, software-pipelined: the next pair's LDS reads
+        // are in flight while the current pair's 8 MFMAs run (pairs past the
+        // valid fragments are read, harmlessly, but not computed)
+        constexpr int NP = (MF + 1) / 2;
+        auto read_pair = [&](int g, bf16x8_t* af) {
 #pragma unroll
-        for (int hf = 0; hf < NH; ++hf) {
-          if (mfw > HF * hf) {
-            bf16x8_t af[HF];
+          for (int u = 0; u < 2; ++u)
+            af[u] = __builtin_bit_cast(bf16x8_t, pa[16 * min(2 * g + u, MF - 1) * kRowSlots]);
+        };
+        bf16x8_t acur[2], anxt[2];
+        read_pair(0, acur);
 #pragma unroll
-            for (int m = 0; m < HF; ++m) af[m] = __builtin_bit_cast(bf16x8_t, pa[16 * (HF * hf + m) * kRowSlots]);
+        for (int g = 0; g < NP; ++g) {
+          if (g + 1 < NP) read_pair(g + 1, anxt);
+          if (2 * g < mfw) {
 #pragma unroll
-            for (int m = 0; m < HF; ++m)
+            for (int u = 0; u < 2; ++u)
+              if (2 * g + u < MF)
 #pragma unroll
-              for (int f = 0; f < 4; ++f) acc[HF * hf + m][f] = mfma16(af[m], bfr[f], acc[HF * hf + m][f]);
+                for (int f = 0; f < 4; ++f) acc[2 * g + u][f] = mfma16(acur[u], bfr[f], acc[2 * g + u][f]);
           }
+          acur[0] = anxt[0];
+          acur[1] = anxt[1];
         }
       }
     };
