@@ -242,17 +242,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
         bfr[f] = read_frag(blo, bhi, fr);
         sb[f] = PT ? 127 : psb[fr] >> bsh;   // byte 0 = this lane's block scale (upper bytes ignored)
       }
+      if (MODE == 0 && !PT) {
+        // MX Gate-Up: its requantising epilogue leaves no registers for a
+        // second fragment row in flight
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          if (m < mfw) {
+            const i32x8_t af = read_frag(alo, ahi, 16 * m);
+            const int sa = psa[16 * m] >> bsh;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[m][f] = mfma_mx(af, bfr[f], acc[m][f], sa, sb[f]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
+      // software-pipelined: fragment row m+1 is read from LDS while row m's
+      // four MFMAs run (rows past the valid ones are read, harmlessly, but
+      // not computed)
+      i32x8_t acur = read_frag(alo, ahi, 0);
+      int sacur = PT ? 127 : psa[0] >> bsh;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        if (m < mfw) {
-          const i32x8_t af = read_frag(alo, ahi, 16 * m);
-          const int sa = PT ? 127 : psa[16 * m] >> bsh;
-#pragma unroll
-          for (int f = 0; f < 4; ++f) acc[m][f] = mfma_mx(af, bfr[f], acc[m][f], sa, sb[f]);
+        i32x8_t anxt = acur;
+        int sanxt = sacur;
+        if (m + 1 < 8) {
+          anxt = read_frag(alo, ahi, 16 * (m + 1));
+          sanxt = PT ? 127 : psa[16 * (m + 1)] >> bsh;
         }
-        // one fragment row's operands live at a time (the second wave on the
-        // SIMD keeps the matrix core busy meanwhile)
+        if (m < mfw) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[m][f] = mfma_mx(acur, bfr[f], acc[m][f], sacur, sb[f]);
+        }
+        // at most two fragment rows' operands live at a time
         __builtin_amdgcn_sched_barrier(0);
+        acur = anxt;
+        sacur = sanxt;
       }
     };
 

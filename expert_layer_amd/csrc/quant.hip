@@ -165,7 +165,9 @@ __global__ void zero_words(unsigned* p, int64_t n) {
     p[i] = 0u;
 }
 
-// amax[m] |= max |x| over tensor m (blockIdx.y); amax starts at 0
+// amax[m] |= max |x| over tensor m (blockIdx.y); amax starts at 0.  Four
+// 8-value loads per thread are in flight per iteration, so a grid of a few
+// hundred workgroups (one same-address atomic each) streams at full rate.
 template <int F32>
 __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, int64_t n,
                                                           unsigned* __restrict__ amax) {
@@ -173,7 +175,18 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
   const int64_t m = blockIdx.y;
   const void* base = tensor_base<F32>(x, m, n);
   float mx = 0.0f;
-  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+  const int64_t step = (int64_t)gridDim.x * 256 * 8;
+  int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  for (; i + 3 * step < n; i += 4 * step) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<F32>(base, i + u * step, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[u][j]));
+  }
+  for (; i < n; i += step) {
     float v[8];
     load8<F32>(base, i, v);
 #pragma unroll
@@ -211,8 +224,9 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* __restric
   }
 }
 
-dim3 tensor_grid(int64_t mats, int64_t n) {
-  const int64_t per = std::min<int64_t>((n + 2047) / 2048, std::max<int64_t>(1, 2048 / std::max<int64_t>(1, mats)));
+// workgroups per tensor: at most `total` over all tensors, none idle
+dim3 tensor_grid(int64_t mats, int64_t n, int64_t total) {
+  const int64_t per = std::min<int64_t>((n + 2047) / 2048, std::max<int64_t>(1, total / std::max<int64_t>(1, mats)));
   return dim3((unsigned)std::max<int64_t>(1, per), (unsigned)mats);
 }
 
@@ -221,7 +235,7 @@ dim3 tensor_grid(int64_t mats, int64_t n) {
 hipError_t launch_tensor_amax(const void* x, int f32, int64_t mats, int64_t n, float* amax, hipStream_t s) {
   unsigned* a = reinterpret_cast<unsigned*>(amax);
   zero_words<<<(unsigned)std::min<int64_t>((mats + 255) / 256, 64), 256, 0, s>>>(a, mats);
-  const dim3 grid = tensor_grid(mats, n);
+  const dim3 grid = tensor_grid(mats, n, 512);
   if (f32)
     tensor_amax_kernel<1><<<grid, 256, 0, s>>>(x, n, a);
   else
@@ -231,7 +245,7 @@ hipError_t launch_tensor_amax(const void* x, int f32, int64_t mats, int64_t n, f
 
 hipError_t launch_quant_tensor(const void* x, int f32, int64_t mats, int64_t n, const float* amax, uint8_t* q,
                                float* sc, hipStream_t s) {
-  const dim3 grid = tensor_grid(mats, n);
+  const dim3 grid = tensor_grid(mats, n, 2048);
   if (f32)
     quant_tensor_kernel<1><<<grid, 256, 0, s>>>(x, n, amax, q, sc);
   else
