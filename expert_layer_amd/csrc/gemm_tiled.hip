@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
     const int g = lo;
     const int mtg = tab.prefix[g + 1] - tab.prefix[g];
     const int local = (int)(it - (int64_t)tab.prefix[g] * NT);
-    const int nt = local / mtg, mt = local % mtg;
+    int mt, nt;
+    item_tile<kBand>(local, mtg, NT, mt, nt);
     const int cnt = a.offsets[g + 1] - a.offsets[g];
     int rs, nrows;
     tile_rows<TM>(cnt, mt, rs, nrows);

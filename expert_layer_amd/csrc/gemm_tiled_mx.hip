@@ -131,7 +131,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
     const int g = lo;
     const int mtg = tab.prefix[g + 1] - tab.prefix[g];
     const int local = (int)(it - (int64_t)tab.prefix[g] * NT);
-    const int nt = local / mtg, mt = local % mtg;
+    int mt, nt;
+    item_tile<kBand>(local, mtg, NT, mt, nt);
     const int cnt = a.offsets[g + 1] - a.offsets[g];
     const int rs = mt * kTM;
     const int nrows = min(kTM, cnt - rs);

@@ -73,6 +73,32 @@ __device__ inline int chunk_group(const ChunkTable& tab, int G, int c) {
   return lo;
 }
 
+// Order of a group's items: (row tile mt, column tile nt) of local item
+// `local` among the group's mtg * NT.  Row tiles are taken in bands of BAND;
+// inside a band the row tile varies fastest.  The 32 consecutive items one
+// XCD runs in a round then cover BAND row tiles x 32 / BAND column tiles,
+// whose operand slices that XCD's L2 serves to all of them, instead of every
+// row tile of a large group against one or two column tiles.  Groups of at
+// most BAND row tiles keep the plain row-fastest order.
+constexpr int kBand = 4;   // row tiles per band of the tiled GEMMs' item order
+
+template <int BAND>
+__device__ inline void item_tile(int local, int mtg, int NT, int& mt, int& nt) {
+  const int nb = mtg / BAND;              // full bands
+  const int band_items = BAND * NT;
+  const int band = local / band_items;
+  if (band < nb) {
+    const int r = local - band * band_items;
+    mt = band * BAND + r % BAND;
+    nt = r / BAND;
+  } else {
+    const int rem = mtg - nb * BAND;      // > 0 here
+    const int r = local - nb * band_items;
+    mt = nb * BAND + r % rem;
+    nt = r / rem;
+  }
+}
+
 // Groups of 64+ rows on average go to the LDS-tiled MFMA kernels; up to 16
 // rows on average, the weight-streaming kernels use 16-row chunks.
 inline bool large_groups(const GemmArgs& a) { return a.T * a.k >= (int64_t)a.E * 64; }
