@@ -61,11 +61,10 @@ int check_experts(const moe_experts_t* ex) {
   if (!aligned16(ex->w1) || !aligned16(ex->w3) || !aligned16(ex->w2)) return MOE_EINVAL;
   const bool scaled = ex->wtype != MOE_W_BF16;
   if (scaled && (!ex->s1 || !ex->s3 || !ex->s2)) return MOE_EINVAL;
-  // the MXFP8 Down kernel tiles 256 output columns; its scale rows are read
-  // as 4-byte words
+  // the MXFP8 and per-tensor Down kernels tile 256 output columns, and read
+  // their scales as 4-byte words
   auto a4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-  // the MXFP8 and per-tensor Down kernels tile 256 output columns
-  const bool tiled8 = ex->wtype == MOE_W_MXFP8 || ex->wtype == MOE_W_FP8_TENSOR;
+  const bool tiled8 =ex->wtype == MOE_W_MXFP8 || ex->wtype == MOE_W_FP8_TENSOR;
   if (tiled8 && ex->H % 256 != 0) return MOE_EUNSUPPORTED;
   if (tiled8 && (!a4(ex->s1) || !a4(ex->s3) || !a4(ex->s2))) return MOE_EINVAL;
   if (ex->has_shared) {
@@ -81,6 +80,18 @@ int check_rows(const moe_experts_t* ex, int64_t T, int k) {
   int st = check_route_shape(T, ex->E, k);
   if (st != MOE_OK) return st;
   if (T * k + (int64_t)ex->has_shared * T >= kMaxRows) return MOE_EUNSUPPORTED;
+  // the MXFP8 and per-tensor GEMMs exist only as tiled kernels, whose 32-bit
+  // row offsets bound x and h (the other weight types fall back to the
+  // weight-streaming kernels instead)
+  if (ex->wtype == MOE_W_MXFP8 || ex->wtype == MOE_W_FP8_TENSOR) {
+    GemmArgs a{};
+    a.T = T;
+    a.k = k;
+    a.H = ex->H;
+    a.I = ex->I;
+    a.has_shared = ex->has_shared;
+    if (!tiled_offsets_ok(a)) return MOE_EUNSUPPORTED;
+  }
   return MOE_OK;
 }
 

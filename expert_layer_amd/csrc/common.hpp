@@ -115,6 +115,17 @@ struct GemmArgs {
   const int32_t* slot_pair;  // [P]
 };
 
+// The LDS-tiled kernels address the rows they gather (x for Gate-Up, h for
+// Down) and the rows of a 256-row weight tile with 32-bit element offsets.
+// Shapes past that range go to the weight-streaming kernels (64-bit
+// addressing) or, for the weight types that only have tiled kernels, are
+// refused.
+inline bool tiled_offsets_ok(const GemmArgs& a) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t R = a.T * a.k + (a.has_shared ? a.T : 0);
+  return a.T * a.H < lim && R * a.I < lim && (int64_t)256 * a.H < lim && (int64_t)256 * a.I < lim;
+}
+
 // sync: 8 ints of device scratch for the tiled kernel's round barrier
 hipError_t launch_gemm13_bf16(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GemmArgs& a, const uint16_t* h, void* y, int y_dtype, hipStream_t s);
@@ -130,7 +141,6 @@ hipError_t launch_gemm2_tiled(const GemmArgs& a, const uint16_t* h, void* y, int
 
 // MXFP8 (E8M0 bytes per 32 K): xs [T, H/32], hs [R, I/32]; weight scales in
 // GemmArgs s1/s3/s2 (and the shared ones) point to bytes [rows, K/32]
-bool tiled_mx_gemm2_ok(const GemmArgs& a);
 hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
                             int* sync, hipStream_t s);
 hipError_t launch_gemm2_mx(const GemmArgs& a, const uint8_t* hq, const uint8_t* hs, void* y, int y_dtype,

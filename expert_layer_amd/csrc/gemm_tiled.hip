@@ -332,8 +332,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
 
 // Tiled kernels need the weight-row tile to divide the output width:
 // Gate-Up 2*I % 256 == 0 (I % 128 == 0 always holds), Down H % 256 == 0.
-bool tiled_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0; }
-bool tiled_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
+bool tiled_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0 && tiled_offsets_ok(a); }
+bool tiled_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0 && tiled_offsets_ok(a); }
 
 // Tile height: 288 rows when groups average 224 to 288 rows, so that a
 // typical group fits one tile and streams each weight tile once instead of

@@ -329,8 +329,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
 
 }  // namespace
 
-bool tiled_fp8_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0; }
-bool tiled_fp8_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
+bool tiled_fp8_gemm13_ok(const GemmArgs& a) { return (2 * a.I) % kTN == 0 && tiled_offsets_ok(a); }
+bool tiled_fp8_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0 && tiled_offsets_ok(a); }
 
 hipError_t launch_gemm13_fp8_tiled(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq, float* hs,
                                    hipStream_t s) {

@@ -410,7 +410,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
 
 // The Down kernel needs H % 256 == 0 (weight-row tile); Gate-Up always tiles
 // (2*I % 256 == 0 since I % 128 == 0).
-bool tiled_mx_gemm2_ok(const GemmArgs& a) { return a.H % kTN == 0; }
 
 hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
                             int* sync, hipStream_t s) {

@@ -171,8 +171,10 @@ int moe_quant_tensor_fp8(const void* x, int dtype, int64_t mats, int64_t n, cons
  * codes plus one fp32 scale per matrix (moe_quant_tensor_fp8): s1, s3, s2 [E],
  * ss1, ss3, ss2 [1].  MXFP8 and per-tensor scale pointers must be 4-byte
  * aligned (MOE_EINVAL otherwise) and H a multiple of 256 (MOE_EUNSUPPORTED
- * otherwise).  The struct itself is host memory; the pointers in it are
- * device pointers.
+ * otherwise).  For these two types x [T,H] and h [R,I] must also each hold
+ * fewer than 2^31 elements, and H, I be below 2^23 (MOE_EUNSUPPORTED
+ * otherwise); bf16 and block-scaled fp8 take any such shape.  The struct
+ * itself is host memory; the pointers in it are device pointers.
  */
 typedef struct moe_experts_t {
   int wtype;

@@ -211,7 +211,7 @@ def check_layer(wl, d, y_dtype=torch.float32, check_rows=None):
     else:
         L = orc.Layer(host(d["w1"]), host(d["w3"]), host(d["w2"]), host(d["sw1"]), host(d["sw3"]), host(d["sw2"]))
         ref = orc.layer_rows(L, x, ids_ref, w_ref, rows)
-    out = b.out.float().cpu().numpy()[rows]
+    out = b.out[torch.from_numpy(rows).to(b.out.device)].float().cpu().numpy()
     err = np.abs(out - ref).max()
     scale = np.abs(ref).max()
     tol = TOL[wl.wtype]

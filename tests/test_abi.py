@@ -210,6 +210,24 @@ def test_forward_persistent_validation(L):
     assert L.moe_forward_persistent_status(None, None) == moe.MOE_EINVAL
 
 
+def test_tiled_only_types_refuse_past_32bit_offsets(L):
+    """MXFP8 and per-tensor FP8 have only tiled kernels, whose gathered-row
+    offsets are 32-bit: x [T,H] or h [R,I] with 2^31 elements or more is
+    refused before anything is launched (bf16 and block fp8 take such shapes
+    on the weight-streaming kernels instead)."""
+    g13, g2 = L.moe_gemm13, L.moe_gemm2
+    x, off, sp, h, ws = 0x20000000, 0x21000000, 0x22000000, 0x23000000, 0x30000000
+    T_big = (1 << 31) // 4096 + 1                    # x has more than 2^31 elements at H = 4096
+    for ex in (_experts(wtype=2, H=4096, s1=A, s3=B, s2=C), _experts(wtype=3, H=4096, s1=D, s3=D, s2=D)):
+        assert g13(ctypes.byref(ex), x, D, off, sp, T_big, 1, h, D + 64, ws, 256, None) == moe.MOE_EUNSUPPORTED
+        assert g2(ctypes.byref(ex), h, D, off, T_big, 1, x, 1, None, 0, None) == moe.MOE_EUNSUPPORTED
+        assert L.moe_forward_workspace_bytes(ctypes.byref(ex), T_big, 1, 1) == 0
+    # h [R, I] past 2^31 elements with x inside the range: R = T (k = 1), I = 2^14
+    ex = _experts(wtype=2, H=256, I=1 << 14, s1=A, s3=B, s2=C)
+    T_h = (1 << 31) // (1 << 14) + 1
+    assert g2(ctypes.byref(ex), h, D, off, T_h, 1, x, 1, None, 0, None) == moe.MOE_EUNSUPPORTED
+
+
 def test_per_tensor_validation(L):
     """Per-tensor FP8: the quantiser entry points and weight type 3 refuse bad
     arguments before launching anything."""

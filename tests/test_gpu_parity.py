@@ -282,6 +282,22 @@ def test_layer_configs(name, ydt):
     _free()
 
 
+def test_rows_past_32bit_element_offsets():
+    """x with more than 2^31 elements (600000 tokens of H = 4096).  The tiled
+    kernels address gathered rows with 32-bit element offsets, so such shapes
+    take the weight-streaming kernels, which address in 64 bits.  Checked on
+    a sample that includes the last tokens, whose x rows start past element
+    2^31."""
+    wl = W("huge-x", T=600000, H=4096, E=8, k=1, I=128, shared=0, seed=43)
+    assert wl.T * wl.H > 2 ** 31
+    d = _inputs(wl)
+    edge = [0, (1 << 31) // wl.H - 1, (1 << 31) // wl.H, (1 << 31) // wl.H + 1, wl.T - 2, wl.T - 1]
+    rows = np.unique(np.concatenate([workloads.sample_rows(wl.T, 64, wl.seed), edge])).astype(np.int64)
+    check_layer(wl, d, y_dtype=torch.bfloat16, check_rows=rows)
+    del d
+    _free()
+
+
 @pytest.mark.parametrize("shape", ["streaming", "tiled"])
 def test_graph_replay_matches_eager(shape):
     """The chain captured as a HIP graph: every replay, with eager launches and
