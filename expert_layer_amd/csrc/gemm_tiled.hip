@@ -192,8 +192,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
     // A loads of 8-row groups wholly past the valid rows are skipped (their
     // LDS rows only feed accumulator rows that are never stored)
     const int nq_live = min(NQ, (nrows + 7) / 8);
+    // Down: the column tiles of one row tile (which run side by side on an
+    // XCD and share its h rows) start their K loop 0-3 stages apart, so they
+    // do not all ask L2 for the same lines at once (3-4 % on the Down time;
+    // no gain for Gate-Up).  Only the order of the fp32 k sums changes.
+    const int rot = MODE == 1 ? (nt & 3) % nk : 0;
     auto issue = [&](int kk, i32x4_t* la, i32x4_t* lb) {
-      const int k0 = kk * kTK;
+      const int kr = kk + rot;
+      const int k0 = (kr >= nk ? kr - nk : kr) * kTK;
 #pragma unroll
       for (int i = 0; i < NA; ++i)
         if (wave + 8 * i < nq_live) load_lds16(A + a_off[i] + k0, &la[(wave + 8 * i) * 64]);

@@ -169,7 +169,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
       wsc1 = wsc0;
     }
 
-    auto issue = [&](int kb, i32x4_t* la, i32x4_t* lb, float* ls) {
+    // Down: the column tiles of one row tile start their K loop 0-3 blocks
+    // apart, so they do not all ask L2 for the same h lines at once; every
+    // k-block index (codes, activation and weight scales) is rotated alike
+    const int rot = MODE == 1 ? (nt & 3) % KB : 0;
+    auto rk = [&](int kbi) { return kbi + rot >= KB ? kbi + rot - KB : kbi + rot; };
+    auto issue = [&](int kbi, i32x4_t* la, i32x4_t* lb, float* ls) {
+      const int kb = rk(kbi);
       const int k0 = kb * kTK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
     auto uniform = [](float v) {
       return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
     };
-    float wg = uniform(wsc0[0]), wu = uniform(wsc1[0]);
+    float wg = uniform(wsc0[rk(0)]), wu = uniform(wsc1[rk(0)]);
     issue(0, a0, b0, s0);
     // KB is even when K % 256 == 0; otherwise the loop ends after the first stage of a pair
     for (int kb = 0; kb < KB; kb += 2) {
@@ -244,8 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
       __builtin_amdgcn_s_barrier();
       float gn = 0.f, un = 0.f;
       if (kb + 1 < KB) {
-        gn = wsc0[kb + 1];
-        un = wsc1[kb + 1];
+        gn = wsc0[rk(kb + 1)];
+        un = wsc1[rk(kb + 1)];
         issue(kb + 1, a1, b1, s1);
       }
       compute(wg, wu, a0, b0, s0);
@@ -257,8 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
       gn = 0.f;
       un = 0.f;
       if (kb + 2 < KB) {
-        gn = wsc0[kb + 2];
-        un = wsc1[kb + 2];
+        gn = wsc0[rk(kb + 2)];
+        un = wsc1[rk(kb + 2)];
         issue(kb + 2, a0, b0, s0);
       }
       compute(wg, wu, a1, b1, s1);

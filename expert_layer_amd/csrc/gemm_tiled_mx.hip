@@ -202,7 +202,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
       }
     }
 
-    auto issue = [&](int kb, i32x4_t* la, i32x4_t* lb, int* lsa, int* lsb) {
+    // Down: the column tiles of one row tile start their K loop 0-3 blocks
+    // apart, so they do not all ask L2 for the same h lines at once
+    const int rot = MODE == 1 ? (nt & 3) % KB : 0;
+    auto issue = [&](int kbi, i32x4_t* la, i32x4_t* lb, int* lsa, int* lsb) {
+      const int kr = kbi + rot;
+      const int kb = kr >= KB ? kr - KB : kr;
       const int k0 = kb * kTK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
