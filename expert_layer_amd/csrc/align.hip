@@ -7,7 +7,8 @@
 // ascend), which makes the result unique and bit-reproducible.  LDS atomics
 // only count; positions come from ordered prefix sums:
 //   * the pairs are cut into chunks of kChunk, one workgroup per chunk, and
-//     each chunk into kWaves contiguous segments, one wave per segment;
+//     each chunk into kWaves contiguous segments of equal length (whole
+//     64-pair steps), one wave per segment;
 //   * count:   per (chunk, expert) totals            -> ws[B][E]
 //   * scan:    one workgroup turns ws into per-chunk bases (exclusive over
 //              chunks) and writes counts / offsets (exclusive over experts)
@@ -27,14 +28,24 @@ constexpr int kChunk = 8192;
 constexpr int kSeg = kChunk / kWaves;  // pairs per wave segment (multiple of 64)
 constexpr int kMaxE = 1024;
 
+// Pairs per wave segment of the chunk starting at chunk0: the chunk's pairs
+// split evenly over the waves in whole 64-pair steps (at most kSeg, so the
+// segments never leave the chunk, and together they cover all of it).
+__device__ __forceinline__ int seg_len(int64_t P, int64_t chunk0) {
+  const int64_t n = min((int64_t)kChunk, P - chunk0);
+  const int per = (int)((n + kWaves - 1) / kWaves);
+  return min(kSeg, (per + 63) & ~63);
+}
+
 // wcnt[w][e] (LDS) := number of pairs of expert e in wave w's segment.
 __device__ void count_segments(const int32_t* __restrict__ ids, int64_t P, int64_t chunk0, int E,
                                int* wcnt) {
   for (int i = threadIdx.x; i < kWaves * E; i += kThreads) wcnt[i] = 0;
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t seg0 = chunk0 + (int64_t)wave * kSeg;
-  for (int i = lane; i < kSeg; i += 64) {
+  const int seg = seg_len(P, chunk0);
+  const int64_t seg0 = chunk0 + (int64_t)wave * seg;
+  for (int i = lane; i < seg; i += 64) {
     const int64_t p = seg0 + i;
     if (p < P) atomicAdd(&wcnt[wave * E + ids[p]], 1);
   }
@@ -59,10 +70,11 @@ __device__ void scatter_segments(const int32_t* __restrict__ ids, int64_t P, int
                                  int32_t* __restrict__ pair_slot) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bits = id_bits(E);
-  const int64_t seg0 = chunk0 + (int64_t)wave * kSeg;
+  const int seg = seg_len(P, chunk0);
+  const int64_t seg0 = chunk0 + (int64_t)wave * seg;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int* mine = wcnt + wave * E;
-  for (int i = 0; i < kSeg; i += 64) {
+  for (int i = 0; i < seg; i += 64) {
     const int64_t p = seg0 + i + lane;
     if (seg0 + i >= P) break;  // wave-uniform
     const bool valid = p < P;

@@ -8,37 +8,54 @@
 
 namespace moe355 {
 
-// y terms of one token for 8 columns starting at c, summed in fixed order
+// One y term: 8 columns of slot s as fp32.
 template <int YBF16>
+__device__ __forceinline__ void load_y8(const void* __restrict__ yv, int64_t s, int H, int c, float v[8]) {
+  if (YBF16) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yv) + s * H + c);
+    const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(u[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(yv) + s * H + c);
+    const float4 a0 = p[0], a1 = p[1];
+    v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+    v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+  }
+}
+
+// y terms of one token for 8 columns starting at c, summed in fixed order
+// (fma for j = 0..k-1 ascending, then + the shared term).  BATCH terms are
+// loaded before they are summed, so BATCH loads per lane are in flight; the
+// order of the sum, and so every result bit, does not depend on BATCH.
+template <int YBF16, int BATCH = 1>
 __device__ __forceinline__ void combine8(const void* __restrict__ yv, const int32_t* slot, const float* wt,
                                          int nterm, int k, int64_t P, int64_t t, int H, int c, float acc[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < nterm; ++j) {
-    const bool sh = j == k;
-    const int64_t s = sh ? P + t : (int64_t)slot[j];
-    const float a = sh ? 1.0f : wt[j];
-    float v[8];
-    if (YBF16) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yv) + s * H + c);
-      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int j0 = 0; j0 < nterm; j0 += BATCH) {
+    float v[BATCH][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_to_f32(u[i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(yv) + s * H + c);
-      const float4 a0 = p[0], a1 = p[1];
-      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    for (int u = 0; u < BATCH; ++u) {
+      const int j = j0 + u;
+      if (j < nterm) load_y8<YBF16>(yv, j == k ? P + t : (int64_t)slot[j], H, c, v[u]);
     }
-    if (sh) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    } else {
+    for (int u = 0; u < BATCH; ++u) {
+      const int j = j0 + u;
+      if (j < nterm) {
+        if (j == k) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(a, v[i], acc[i]);
+          for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
+        } else {
+          const float a = wt[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(a, v[u][i], acc[i]);
+        }
+      }
     }
   }
 }
