@@ -42,6 +42,8 @@ SMALL = [
     W("single-expert", T=33, H=128, E=1, k=1, I=128, shared=0, seed=15),
     W("single-token", T=1, H=256, E=16, k=4, I=256, shared=1, seed=16),
     W("wide-E", T=50, H=128, E=1000, k=32, I=128, shared=1, seed=17),
+    # the largest expert count and top-k the ABI accepts
+    W("max-E", T=40, H=128, E=1024, k=32, I=128, shared=1, seed=44),
     W("zipf-bias", T=200, H=256, E=32, k=8, I=128, shared=1, bias="all", seed=18),
     W("mixed-bias", T=200, H=256, E=32, k=8, I=128, shared=1, bias="mix", bias_frac=0.3, seed=19),
     W("router-small", T=100, H=512, E=64, k=8, I=128, shared=1, router=True, bias="mix", bias_frac=0.3, seed=20),

@@ -33,6 +33,7 @@ CASES = [
     W("p-one-expert", T=16, H=128, E=1, k=1, I=128, shared=0, seed=63),
     # 16 logits per lane in the route phase
     W("p-wide-E", T=50, H=128, E=1000, k=32, I=128, shared=1, seed=64),
+    W("p-max-E", T=40, H=128, E=1024, k=32, I=128, shared=1, seed=67),
     W("p-mixed-bias", T=60, H=256, E=32, k=8, I=128, shared=1, bias="mix", bias_frac=0.3, seed=65),
     W("p-router", T=100, H=512, E=64, k=8, I=128, shared=1, router=True, bias="mix", bias_frac=0.3, seed=66),
 ]
