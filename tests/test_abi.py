@@ -263,3 +263,21 @@ def test_router_validation(L):
     assert L.moe_router_gemm(A, B, C, D, 0, 128, 8, None) == moe.MOE_OK
     assert L.moe_router_split(A, B, B, 4, 4, None) == moe.MOE_EINVAL     # hi/lo alias
     assert L.moe_router_split(A, B, C, 0, 4, None) == moe.MOE_OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With no built library the binding raises on first use; there is no
+    other code path that could compute a result instead."""
+    import subprocess
+    import sys
+    code = ("import expert_layer_amd as moe\n"
+            "try:\n"
+            "    moe.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    raise SystemExit('loaded a library that does not exist')\n")
+    env = dict(os.environ, MOE355_LIB=str(tmp_path / "libmoe355.so"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "raised:" in r.stdout and "is not built" in r.stdout
