@@ -246,11 +246,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
         for (int g = 0; g < NP; ++g) {
           if (g + 1 < NP) read_pair(g + 1, anxt);
           if (2 * g < mfw) {
+            // raised wave priority while this wave issues its MFMAs (1-2 %)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
               if (2 * g + u < MF)
 #pragma unroll
                 for (int f = 0; f < 4; ++f) acc[2 * g + u][f] = mfma16(acur[u], bfr[f], acc[2 * g + u][f]);
+            __builtin_amdgcn_s_setprio(0);
           }
           acur[0] = anxt[0];
           acur[1] = anxt[1];

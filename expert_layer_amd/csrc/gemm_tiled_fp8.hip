@@ -218,12 +218,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
           f32x4_t p[4];
 #pragma unroll
           for (int f = 0; f < 4; ++f) p[f] = mfma_fp8(af, bfr[f]);
+          // the promotion runs at raised wave priority, so the SIMD's issue
+          // arbiter serves it ahead of the other wave and the matrix core gets
+          // that wave's next MFMAs sooner (about 3 % on both fp8 kernels)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
             const float ws = (MODE == 0 && f >= 2) ? wu : wg;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[m][f][i] = __builtin_fmaf(xs4[i] * ws, p[f][i], acc[m][f][i]);
           }
+          __builtin_amdgcn_s_setprio(0);
         }
         // keep the partial sums of one fragment row in flight at a time (the
         // second wave on the SIMD fills the matrix core meanwhile)
