@@ -354,11 +354,13 @@ static bool tall_tiles(const GemmArgs& a) {
 }
 
 hipError_t launch_gemm13_tiled(const GemmArgs& a, const uint16_t* x, uint16_t* h, int* sync, hipStream_t s) {
-  clear_sync<<<1, 64, 0, s>>>(sync);
-  if (tall_tiles(a))
-    gemm_tiled<0, 0, 9><<<device_cus(), kThreads, 0, s>>>(a, x, h, sync);
+  const bool tall = tall_tiles(a);
+  int* rb = round_barrier(a, tall ? 288 : 256) ? sync : nullptr;
+  if (rb) clear_sync<<<1, 64, 0, s>>>(rb);
+  if (tall)
+    gemm_tiled<0, 0, 9><<<device_cus(), kThreads, 0, s>>>(a, x, h, rb);
   else
-    gemm_tiled<0, 0, 8><<<device_cus(), kThreads, 0, s>>>(a, x, h, sync);
+    gemm_tiled<0, 0, 8><<<device_cus(), kThreads, 0, s>>>(a, x, h, rb);
   return hipGetLastError();
 }
 

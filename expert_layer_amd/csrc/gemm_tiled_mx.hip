@@ -424,7 +424,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
 hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
                             int* sync, hipStream_t s) {
   clear_sync_mx<<<1, 64, 0, s>>>(sync, nullptr);
-  gemm_tiled_mx<0, 0><<<device_cus(), kThreads, 0, s>>>(a, xq, xs, hq, hs, sync);
+  gemm_tiled_mx<0, 0><<<device_cus(), kThreads, 0, s>>>(a, xq, xs, hq, hs,
+                                                       round_barrier(a, kTM) ? sync : nullptr);
   return hipGetLastError();
 }
 
@@ -432,7 +433,8 @@ hipError_t launch_gemm13_pt(const GemmArgs& a, const uint8_t* xq, const float* x
                             int* sync, hipStream_t s) {
   clear_sync_mx<<<1, 64, 0, s>>>(sync, reinterpret_cast<unsigned*>(hamax));
   gemm_tiled_mx<0, 0, 1><<<device_cus(), kThreads, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
-                                                          reinterpret_cast<uint8_t*>(hamax), sync);
+                                                          reinterpret_cast<uint8_t*>(hamax),
+                                                          round_barrier(a, kTM) ? sync : nullptr);
   return hipGetLastError();
 }
 

@@ -99,6 +99,15 @@ __device__ inline void item_tile(int local, int mtg, int NT, int& mt, int& nt) {
   }
 }
 
+// The Gate-Up tiled kernels' per-XCD round barrier keeps the row tiles that
+// share a weight tile in step through L2.  It pays when groups average at
+// least 1.5 row tiles (router shape, 2 tiles per group: 15 % faster with it);
+// with about one tile per group (prefill) or fewer (the skewed fp8 shapes)
+// the tiles share little and the waits cost 3-6 %, so it is left off.
+inline bool round_barrier(const GemmArgs& a, int tile_rows) {
+  return 2 * a.T * a.k >= (int64_t)3 * a.E * tile_rows;
+}
+
 // Groups of 64+ rows on average go to the LDS-tiled MFMA kernels; up to 16
 // rows on average, the weight-streaming kernels use 16-row chunks.
 inline bool large_groups(const GemmArgs& a) { return a.T * a.k >= (int64_t)a.E * 64; }
