@@ -30,12 +30,12 @@
 // workgroup per CU strides over them, and the physical workgroup -> worker
 // mapping keeps consecutive workers on the same XCD (workgroups are dealt to
 // the 8 XCDs round robin), so m-tiles that share a weight tile share that
-// XCD's L2.  In the Gate-Up kernel the workgroups of one XCD also meet at a
-// counter in the caller's workspace after every round of items, so the
-// items that share an A tile or a weight tile start together and stream the
-// same lines through L2 at about the same time (measured: fewer L2 misses,
-// Gate-Up 4-8% faster).  The wait is bounded, so the barrier only ever
-// affects timing, never results.
+// XCD's L2.  Where groups span two or more row tiles, the workgroups of one
+// XCD also meet at a counter in the caller's workspace after every round of
+// Gate-Up items, so the items that share a weight tile start together and
+// stream the same lines through L2 at about the same time (router shape:
+// 15 % faster; with one tile per group the waits cost more than they save).
+// The wait is bounded, so the barrier only ever affects timing, never results.
 #include "tiles.hpp"
 
 namespace moe355 {
