@@ -300,14 +300,21 @@ def test_rows_past_32bit_element_offsets():
     _free()
 
 
-@pytest.mark.parametrize("shape", ["streaming", "tiled"])
+GRAPH_SHAPES = {
+    "streaming": W("graph-s", T=64, H=512, E=64, k=8, I=256, shared=1, seed=41),
+    "tiled": W("graph-t", T=500, H=512, E=32, k=8, I=256, shared=1, bias="mix", bias_frac=0.3, seed=42),
+    # the fp8 chains add the quantisation passes and their cleared counters
+    "fp8": W("graph-f8", T=500, H=512, E=32, k=8, I=256, shared=1, wtype="fp8", bias="mix", bias_frac=0.3, seed=45),
+    "mxfp8": W("graph-mx", T=500, H=512, E=32, k=8, I=256, shared=1, wtype="mxfp8", seed=46),
+    "fp8t": W("graph-pt", T=500, H=512, E=32, k=8, I=256, shared=1, wtype="fp8t", seed=47),
+}
+
+
+@pytest.mark.parametrize("shape", list(GRAPH_SHAPES))
 def test_graph_replay_matches_eager(shape):
     """The chain captured as a HIP graph: every replay, with eager launches and
     synchronisations between replays, gives the eager result bit for bit."""
-    if shape == "streaming":
-        wl = W("graph-s", T=64, H=512, E=64, k=8, I=256, shared=1, seed=41)
-    else:
-        wl = W("graph-t", T=500, H=512, E=32, k=8, I=256, shared=1, bias="mix", bias_frac=0.3, seed=42)
+    wl = GRAPH_SHAPES[shape]
     d = _inputs(wl)
     layer, b, _ = run_gpu(wl, d)
     want = b.out.clone()
