@@ -211,11 +211,13 @@ typedef struct moe_experts_t {
  * offsets, slot_pair: from moe_align.
  * ws: device scratch of moe_gemm_workspace_bytes bytes, 4-byte aligned; its
  *   contents need not be initialised (the call clears what it uses, on its
- *   stream).  The bf16 kernel for large groups and the MXFP8 kernel keep one counter per XCD in
- *   it, at which the workgroups of that XCD meet after every round of tiles
- *   so that tiles sharing operands stream them through L2 together.  The
- *   waits are bounded, so the workspace affects timing only, never results;
- *   calls that may run concurrently should still use separate workspaces.
+ *   stream).  The tiled Gate-Up kernels (bf16, MXFP8, per-tensor) may keep
+ *   one counter per XCD in it, at which the workgroups of that XCD meet after
+ *   every round of tiles so that tiles sharing a weight tile stream it
+ *   through L2 together (used where groups average 1.5 row tiles or more).
+ *   The waits are bounded, so the workspace affects timing only, never
+ *   results; calls that may run concurrently should still use separate
+ *   workspaces.  The per-tensor Gate-Up also clears the h amax word in hs.
  *   ws NULL or smaller than the query: MOE_EWORKSPACE; ws overlapping x or h
  *   or misaligned: MOE_EINVAL.
  */
