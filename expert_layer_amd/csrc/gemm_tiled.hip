@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
   __shared__ ChunkTable tab;
 
   const int G = a.E + (a.has_shared ? 1 : 0);
-  const int nmt_total = build_chunks(tab, a.offsets, G, TM);
+  const int nmt_total = MODE == 1 ? build_chunks_sf(tab, a.offsets, G, a.E, a.has_shared, TM)
+                                   : build_chunks(tab, a.offsets, G, TM);
   const int H = a.H, I = a.I;
   const int K = MODE == 0 ? H : I;            // reduction length
   const int NT = MODE == 0 ? (2 * I) / kTN : H / kTN;
@@ -139,9 +140,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled(GemmArgs a, const uint
       const int mid = (lo + hi + 1) >> 1;
       if ((int64_t)tab.prefix[mid] * NT <= it) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
-    const int mtg = tab.prefix[g + 1] - tab.prefix[g];
-    const int local = (int)(it - (int64_t)tab.prefix[g] * NT);
+    const int mtg = tab.prefix[lo + 1] - tab.prefix[lo];
+    const int local = (int)(it - (int64_t)tab.prefix[lo] * NT);
+    const int g = MODE == 1 ? sf_group(lo, a.E, a.has_shared) : lo;
     int mt, nt;
     item_tile<kBand>(local, mtg, NT, mt, nt);
     const int cnt = a.offsets[g + 1] - a.offsets[g];

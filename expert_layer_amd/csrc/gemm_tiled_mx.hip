@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
   __shared__ ChunkTable tab;
 
   const int G = a.E + (a.has_shared ? 1 : 0);
-  const int nmt_total = build_chunks(tab, a.offsets, G, kTM);
+  const int nmt_total = MODE == 1 ? build_chunks_sf(tab, a.offsets, G, a.E, a.has_shared, kTM)
+                                   : build_chunks(tab, a.offsets, G, kTM);
   const int H = a.H, I = a.I;
   const int K = MODE == 0 ? H : I;
   const int KB = K / kTK;                 // stages
@@ -128,9 +129,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
       const int mid = (lo + hi + 1) >> 1;
       if ((int64_t)tab.prefix[mid] * NT <= it) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
-    const int mtg = tab.prefix[g + 1] - tab.prefix[g];
-    const int local = (int)(it - (int64_t)tab.prefix[g] * NT);
+    const int mtg = tab.prefix[lo + 1] - tab.prefix[lo];
+    const int local = (int)(it - (int64_t)tab.prefix[lo] * NT);
+    const int g = MODE == 1 ? sf_group(lo, a.E, a.has_shared) : lo;
     int mt, nt;
     item_tile<kBand>(local, mtg, NT, mt, nt);
     const int cnt = a.offsets[g + 1] - a.offsets[g];

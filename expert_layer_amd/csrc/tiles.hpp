@@ -60,6 +60,55 @@ __device__ inline int build_chunks(ChunkTable& tab, const int32_t* __restrict__ 
   return tab.prefix[G];
 }
 
+// The tiled Down kernels order their items with the shared expert's group
+// (index E) first: slot vg of the order holds group vg - 1 (vg >= 1), slot 0
+// the shared group, and prefix[] is built over that order.  The shared group
+// is the largest one with full tiles, so the partly filled last round of
+// items then holds small routed groups instead (Down 2-2.5 % faster; the
+// Gate-Up kernels measured 1 % slower with it and keep the plain order).
+__device__ __forceinline__ int sf_group(int vg, int E, int has_shared) {
+  return has_shared ? (vg == 0 ? E : vg - 1) : vg;
+}
+__device__ inline int build_chunks_sf(ChunkTable& tab, const int32_t* __restrict__ offsets, int G, int E,
+                                      int has_shared, int chunk_rows) {
+  const int nthreads = blockDim.x;
+  const int per = (G + nthreads - 1) / nthreads;
+  const int g0 = threadIdx.x * per;
+  int local = 0;
+  for (int vg = g0; vg < g0 + per && vg < G; ++vg) {
+    const int g = sf_group(vg, E, has_shared);
+    const int rows = offsets[g + 1] - offsets[g];
+    local += (rows + chunk_rows - 1) / chunk_rows;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int v = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int n = __shfl_up(v, off);
+    if (lane >= off) v += n;
+  }
+  if (lane == 63) tab.wsum[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < (nthreads + 63) / 64; ++w) {
+      const int c = tab.wsum[w];
+      tab.wsum[w] = run;
+      run += c;
+    }
+    tab.prefix[G] = run;
+  }
+  __syncthreads();
+  int run = v - local + tab.wsum[wave];
+  for (int vg = g0; vg < g0 + per && vg < G; ++vg) {
+    tab.prefix[vg] = run;
+    const int g = sf_group(vg, E, has_shared);
+    const int rows = offsets[g + 1] - offsets[g];
+    run += (rows + chunk_rows - 1) / chunk_rows;
+  }
+  __syncthreads();
+  return tab.prefix[G];
+}
+
 // Group owning chunk c: the last g with prefix[g] <= c (empty groups skipped).
 __device__ inline int chunk_group(const ChunkTable& tab, int G, int c) {
   int lo = 0, hi = G - 1;
