@@ -25,12 +25,12 @@
 // 16-row fragments past the tile's valid rows are skipped.  A group with r
 // rows is cut into full TM-row tiles and a remainder tile.
 //
-// Items (m-tile, n-tile) are ordered group by group, n-tile by n-tile, with
-// the m-tiles of one (group, n-tile) adjacent; a persistent grid of one
-// workgroup per CU strides over them, and the physical workgroup -> worker
-// mapping keeps consecutive workers on the same XCD (workgroups are dealt to
-// the 8 XCDs round robin), so m-tiles that share a weight tile share that
-// XCD's L2.  Where groups span two or more row tiles, the workgroups of one
+// Items (m-tile, n-tile) are ordered group by group (the Down kernel takes
+// the shared expert's group first), inside a group in bands of 4 m-tiles with
+// the m-tile fastest; a persistent grid of one workgroup per CU strides over
+// them, and the physical workgroup -> worker mapping keeps consecutive
+// workers on the same XCD (workgroups are dealt to the 8 XCDs round robin),
+// so m-tiles that share a weight tile share that XCD's L2.  Where groups span two or more row tiles, the workgroups of one
 // XCD also meet at a counter in the caller's workspace after every round of
 // Gate-Up items, so the items that share a weight tile start together and
 // stream the same lines through L2 at about the same time (router shape:
