@@ -310,6 +310,34 @@ GRAPH_SHAPES = {
 }
 
 
+def _random_shapes(n, seed):
+    """Seeded random layer shapes across weight types, sizes, top-k, shared
+    expert and bias mode (every row checked when T <= 512)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wtype = ["bf16", "fp8", "mxfp8", "fp8t"][i % 4]
+        E = int(rng.choice([1, 3, 8, 16, 40, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 7, 64, 200, 513]))
+        step = 256 if wtype in ("mxfp8", "fp8t") else 128
+        H = step * int(rng.integers(1, 5))
+        I = 128 * int(rng.integers(1, 4))
+        shared = int(rng.integers(0, 2))
+        bias = str(rng.choice(["none", "all", "mix"]))
+        out.append(W(f"rand{i}-{wtype}-T{T}-E{E}-k{k}-H{H}-I{I}-S{shared}-{bias}", T=T, H=H, E=E, k=k, I=I,
+                     shared=shared, wtype=wtype, bias=bias, bias_frac=0.3, seed=5000 + i))
+    return out
+
+
+RANDOM = _random_shapes(48, 2024)
+
+
+@pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
+def test_random_shapes(wl):
+    check_layer(wl, _inputs(wl), y_dtype=torch.float32 if wl.T < 200 else torch.bfloat16)
+
+
 @pytest.mark.parametrize("shape", list(GRAPH_SHAPES))
 def test_graph_replay_matches_eager(shape):
     """The chain captured as a HIP graph: every replay, with eager launches and
