@@ -126,3 +126,31 @@ def test_persistent_repeats_and_graph_replay():
         moe.moe_forward_persistent(layer.experts, d["x"], wl.k, out, ws, **kw)    # eager between replays
         moe.moe_forward_persistent_status(ws)
         assert torch.equal(out, want), f"eager after replay {i}"
+
+
+def _random_shapes(n, seed):
+    """Seeded random shapes inside the persistent kernel's envelope (bf16,
+    T*k <= 16*E): expert count, top-k, widths, shared expert, bias mode and
+    the device router drawn at random."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 5, 16, 48, 64, 200]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 16 * E // k + 1))
+        H = 128 * int(rng.integers(1, 6))
+        I = 128 * int(rng.integers(1, 5))
+        shared = int(rng.integers(0, 2))
+        bias = str(rng.choice(["none", "all", "mix"]))
+        router = bool(rng.integers(0, 4) == 0)
+        out.append(W(f"prand{i}-T{T}-E{E}-k{k}-H{H}-I{I}-S{shared}-{bias}{'-router' if router else ''}", T=T,
+                     H=H, E=E, k=k, I=I, shared=shared, bias=bias, bias_frac=0.3, router=router, seed=7000 + i))
+    return out
+
+
+RANDOM = _random_shapes(16, 2025)
+
+
+@pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
+def test_persistent_random_shapes(wl):
+    test_persistent_matches_chain_and_oracle(wl, moe.MOE_DTYPE_F32 if wl.T % 2 else moe.MOE_DTYPE_BF16)
