@@ -151,8 +151,9 @@ def test_per_tensor_quantiser_over_bf16_and_f32():
         scaled = vals * np.ldexp(1.0, rng.integers(-40, 40, size=(vals.shape[0], 1))).astype(np.float32)
     scaled = np.where(np.abs(scaled) < 3.0e38, scaled, 0.0).astype(np.float32)
     scaled_bits = torch.from_numpy(scaled).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    f32 = np.where(np.abs(scaled) < 1e30, scaled * rng.standard_normal(scaled.shape).astype(np.float32), 0.0)
-    f32 = f32.astype(np.float32)
+    keep = np.abs(scaled) < 1e30
+    small = np.where(keep, scaled, 0.0).astype(np.float32)     # so the product cannot overflow
+    f32 = np.where(keep, small * rng.standard_normal(scaled.shape).astype(np.float32), 0.0).astype(np.float32)
     for data in (rows, scaled_bits, f32):
         mats = data.shape[0]
         if data.dtype == np.float32:
