@@ -21,6 +21,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A build of a modified copy of the source, loaded instead of liboracle.so: the
+# mutation test uses it to check that the pins catch planted mistakes.
+_LIB_OVERRIDE = os.environ.get("MOE355_ORACLE_LIB")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -49,9 +52,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB)
         L.orc_bf16_value.restype = ctypes.c_double
         L.orc_bf16_value.argtypes = [ctypes.c_uint16]
         L.orc_bf16_nearest.restype = ctypes.c_uint16
