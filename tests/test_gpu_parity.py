@@ -367,6 +367,46 @@ def test_graph_replay_matches_eager(shape):
         assert torch.equal(b.out, want), f"eager after replay {i}"
 
 
+def test_concurrent_streams_match_serial():
+    """The library keeps no state between calls: two layers (tiled kernels with
+    the per-XCD round barrier, whose counters live in the workspace, and
+    weight-streaming kernels) run at the same time on two streams, each with
+    its own workspace, and give their serial outputs bit for bit."""
+    import expert_layer_amd as moe
+    from expert_layer_amd.chain import Layer
+    shapes = [W("cc-tiled", T=4096, H=512, E=8, k=4, I=256, shared=1, bias="mix", bias_frac=0.3, seed=81),
+              W("cc-stream", T=64, H=1024, E=64, k=8, I=256, shared=1, seed=82)]
+    runs = []
+    for wl in shapes:
+        log(f"concurrent {wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I}")
+        d = _inputs(wl)
+        layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"])
+        ydt = moe.MOE_DTYPE_F32
+        ws = torch.empty(moe.moe_forward_workspace_bytes(layer.experts, wl.T, wl.k, ydt), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        kw = dict(logits=d["logits"], bias=d["bias"], bias_rows=d["bias_rows"], y_dtype=ydt,
+                  topk_ids=torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda"),
+                  topk_w=torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda"))
+        runs.append((wl, layer, d["x"], ws, out, kw))
+    want = []
+    for wl, layer, x, ws, out, kw in runs:
+        moe.moe_forward(layer.experts, x, wl.k, out, ws, **kw)
+        torch.cuda.synchronize()
+        want.append(out.clone())
+    streams = [torch.cuda.Stream() for _ in runs]
+    for rep in range(3):
+        for run in runs:
+            run[4].zero_()
+        for s, (wl, layer, x, ws, out, kw) in zip(streams, runs):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                moe.moe_forward(layer.experts, x, wl.k, out, ws, **kw)
+        torch.cuda.synchronize()
+        for (wl, _, _, _, out, _), ref in zip(runs, want):
+            assert torch.equal(out, ref), f"{wl.name}, repeat {rep}"
+
+
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16], ids=["yf32", "ybf16"])
 def test_combine_rmsnorm_stage(ydt):
     """combine + residual + RMSNorm on the GPU's own y against the oracle's
