@@ -214,16 +214,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
         const int fr = MODE == 0 ? (f < 2 ? 16 * f : kTN / 2 + 16 * (f - 2)) : 16 * f;  // relative to brow0
         bfr[f] = read_frag(blo, bhi, fr);
       }
-      // Gate-Up: the next fragment row's x fragment and scale are read while
-      // this row's MFMAs run and its partials are promoted (4-6 % on the
-      // Gate-Up; the extra registers spill 24 bytes of per-item addressing,
-      // reloaded once per item, nothing inside the K loop)
+      // the next fragment row's x fragment (Gate-Up: and its scale) is read
+      // while this row's MFMAs run and its partials are promoted (Gate-Up 4-6 %
+      // faster, where the extra registers spill 24 bytes of per-item
+      // addressing, reloaded once per item, nothing inside the K loop; Down
+      // 2-3 %, no spill)
       i32x8_t af_next = read_frag(alo, ahi, 0);
       float xs_next = lsw[0];
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (m < mfw) {
-          const i32x8_t af = MODE == 0 ? af_next : read_frag(alo, ahi, 16 * m);
+          const i32x8_t af = af_next;
           // the four block products first, then their promotion: each fma waits
           // only for an MFMA issued three or more slots earlier
           f32x4_t p[4];
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_fp8(GemmArgs a, const 
             __builtin_amdgcn_s_setprio(0);
           } else {
             const f32x4_t xs4 = *reinterpret_cast<const f32x4_t*>(&lsw[16 * m]);
+            if (m + 1 < 8) af_next = read_frag(alo, ahi, 16 * (m + 1));
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int f = 0; f < 4; ++f)
