@@ -311,17 +311,30 @@ void orc_quant_blocks_fp8(const uint16_t* w, int64_t mats, int rows, int cols, u
 // per-tensor scales): mats tensors of n values each, bf16 bit patterns
 // (f32 = 0) or fp32 values (f32 = 1).  s[m] = amax / 448 (fp32, 1 if amax is
 // 0), q = e4m3(fp32(v / s[m])).
-void orc_quant_tensor_fp8(const void* x, int f32, int64_t mats, int64_t n, uint8_t* q, float* s) {
+// The work is split over nthreads threads in contiguous pieces; a maximum does
+// not depend on the order it is taken in, so the result is the same for any
+// thread count.
+void orc_quant_tensor_fp8(const void* x, int f32, int64_t mats, int64_t n, uint8_t* q, float* s, int nthreads) {
   auto val = [&](int64_t i) -> float {
     if (f32) return static_cast<const float*>(x)[i];
     return static_cast<float>(bf16_value(static_cast<const uint16_t*>(x)[i]));
   };
+  const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(nthreads, (n + 65535) / 65536));
+  const int64_t len = (n + pieces - 1) / pieces;
+  std::vector<float> part(pieces);
   for (int64_t m = 0; m < mats; ++m) {
+    parallel_for(pieces, nthreads, [&](int64_t p) {
+      float pmax = 0.0f;
+      for (int64_t i = p * len; i < std::min(n, (p + 1) * len); ++i) pmax = std::max(pmax, std::fabs(val(m * n + i)));
+      part[p] = pmax;
+    });
     float amax = 0.0f;
-    for (int64_t i = 0; i < n; ++i) amax = std::max(amax, std::fabs(val(m * n + i)));
+    for (int64_t p = 0; p < pieces; ++p) amax = std::max(amax, part[p]);
     const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
     s[m] = sc;
-    for (int64_t i = 0; i < n; ++i) q[m * n + i] = e4m3_code(val(m * n + i) / sc);
+    parallel_for(pieces, nthreads, [&](int64_t p) {
+      for (int64_t i = p * len; i < std::min(n, (p + 1) * len); ++i) q[m * n + i] = e4m3_code(val(m * n + i) / sc);
+    });
   }
 }
 
@@ -389,12 +402,24 @@ static double mx_dot(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, co
 }
 
 // Per-tensor fp8 dot product of code rows: sum_k dec(xq[k]) * dec(wq[k]) over
-// the whole K (the scales multiply the result once).
+// the whole K (the scales multiply the result once).  Every E4M3 value is an
+// integer multiple of 2^-9 below 2^9, so each product is a multiple of 2^-18
+// below 2^18 and, for K < 2^17, every partial sum is a multiple of 2^-18 below
+// 2^35: exact in double whatever the order of the additions.
 static double tensor_dot(const uint8_t* xq, const uint8_t* wq, int K) {
   const double* dec = e4m3_table();
   double acc = 0.0;
   for (int i = 0; i < K; ++i) acc += dec[xq[i]] * dec[wq[i]];
   return acc;
+}
+
+// Per-tensor fp8 h of one (token, expert) column from the code dot products of
+// the gate and up rows: g = gdot * xs * s1, u = udot * xs * s3 (scaled once),
+// h = SiLU(g) * u rounded to fp32.
+static float pt_h(double gdot, double udot, double xsc, double s1, double s3) {
+  const double gv = gdot * xsc * s1;
+  const double uv = udot * xsc * s3;
+  return static_cast<float>(silu(gv) * uv);
 }
 
 // One SwiGLU expert on one token with FP8 operands (the "activation
@@ -466,9 +491,24 @@ struct orc_layer {
 // The arithmetic per (token, expert) is exactly orc_expert_bf16 /
 // orc_expert_fp8; the loops only run expert by expert so that each expert's
 // weight rows are read once for all the checked tokens that use it.
-void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int32_t* ids,
-                    const double* weights, int k, const int64_t* rows, int64_t nrows, double* out,
-                    int nthreads) {
+//
+// orc_layer_rows_trace also hands out the intermediate h of every pair it
+// computes (tr, any member may be NULL), pair q = r * (k + S) + j for rank j < k
+// of token rows[r] and j == k for its shared expert:
+//   h       [npairs, I] fp32: h rounded to fp32 (the value the FP8 paths requantise)
+//   hq      [npairs, I] the requantised h codes (FP8 paths)
+//   hs      [npairs, I/128] fp32 scales (block FP8) or [npairs, I/32] E8M0 bytes (MXFP8)
+//   h_scale [1] the scale of the whole h (per-tensor FP8)
+struct orc_trace {
+  float* h;
+  uint8_t* hq;
+  void* hs;
+  float* h_scale;
+};
+
+void orc_layer_rows_trace(const orc_layer* L, const void* x, const void* xs, const int32_t* ids,
+                          const double* weights, int k, const int64_t* rows, int64_t nrows, double* out,
+                          int nthreads, const orc_trace* tr) {
   const int H = L->H, I = L->I, E = L->E;
   const int hb = H / 128, ib = I / 128;
   const int64_t mat = (int64_t)I * H;
@@ -509,7 +549,7 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
     for (int64_t q : members[g]) {
       const int64_t t = token_of(q);
       for (int n = n0; n < n0 + 128; ++n) {
-        double gv, uv;
+        double gv = 0.0, uv = 0.0;
         if (!fp8) {
           const uint16_t* xr = static_cast<const uint16_t*>(x) + t * H;
           const uint16_t* w1 = (sh ? static_cast<const uint16_t*>(L->sw1) : static_cast<const uint16_t*>(L->w1) + g * mat) + (int64_t)n * H;
@@ -536,8 +576,7 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
             const double xsc = fs(xs)[0];
             const double s1 = sh ? fs(L->ss1)[0] : fs(L->s1)[g];
             const double s3 = sh ? fs(L->ss3)[0] : fs(L->s3)[g];
-            gv = tensor_dot(xr, w1, H) * xsc * s1;
-            uv = tensor_dot(xr, w3, H) * xsc * s3;
+            hbuf[q * I + n] = pt_h(tensor_dot(xr, w1, H), tensor_dot(xr, w3, H), xsc, s1, s3);
           } else {
             const float* xsr = fs(xs) + t * hb;
             const float* s1 = (sh ? fs(L->ss1) : fs(L->s1) + g * blk) + (n / 128) * hb;
@@ -545,7 +584,7 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
             gv = fp8_dot(xr, xsr, w1, s1, H);
             uv = fp8_dot(xr, xsr, w3, s3, H);
           }
-          hbuf[q * I + n] = static_cast<float>(silu(gv) * uv);
+          if (!pt) hbuf[q * I + n] = static_cast<float>(silu(gv) * uv);
         }
       }
     }
@@ -585,6 +624,15 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
           hq[q * I + gi * 128 + i] = e4m3_code(static_cast<float>(hbuf[q * I + gi * 128 + i]) / sc);
       }
     });
+  }
+
+  if (tr) {
+    if (tr->h)
+      for (int64_t i = 0; i < npairs * (int64_t)I; ++i) tr->h[i] = static_cast<float>(hbuf[i]);
+    if (tr->hq && fp8) std::memcpy(tr->hq, hq.data(), hq.size());
+    if (tr->hs && mx) std::memcpy(tr->hs, hsm.data(), hsm.size());
+    if (tr->hs && fp8 && !mx && !pt) std::memcpy(tr->hs, hs.data(), hs.size() * sizeof(float));
+    if (tr->h_scale && pt) *tr->h_scale = h_tensor_scale;
   }
 
   // phase 2: y = h.w2^T for every pair, task = (group, 128 rows of w2)
@@ -629,6 +677,19 @@ void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int
       for (int m = 0; m < H; ++m) o[m] += wt * ybuf[q * H + m];
     }
   });
+}
+
+void orc_layer_rows(const orc_layer* L, const void* x, const void* xs, const int32_t* ids,
+                    const double* weights, int k, const int64_t* rows, int64_t nrows, double* out,
+                    int nthreads) {
+  orc_layer_rows_trace(L, x, xs, ids, weights, k, rows, nrows, out, nthreads, nullptr);
+}
+
+// Per-tensor FP8 h of n (token, column) entries of one expert from the exact
+// code dot products of its gate rows (gdot) and up rows (udot): the arithmetic
+// of the layer's Gate-Up step above, for a whole-tensor pass over h.
+void orc_pt_h(const double* gdot, const double* udot, int64_t n, double xsc, double s1, double s3, float* h) {
+  for (int64_t i = 0; i < n; ++i) h[i] = pt_h(gdot[i], udot[i], xsc, s1, s3);
 }
 
 // ---------------------------------------------------------------- combine / norm

@@ -46,6 +46,10 @@ class _Layer(ctypes.Structure):
                 ("h_scale", _P)]
 
 
+class _Trace(ctypes.Structure):
+    _fields_ = [("h", _P), ("hq", _P), ("hs", _P), ("h_scale", _P)]
+
+
 _lib = None
 
 
@@ -77,10 +81,13 @@ def lib():
         L.orc_quant_rows_mx.argtypes = [_P, _I64, _I32, _P, _P, _I32]
         L.orc_quant_rows_mx_f32.argtypes = [_P, _I64, _I32, _P, _P]
         L.orc_quant_blocks_fp8.argtypes = [_P, _I64, _I32, _I32, _P, _P, _I32]
-        L.orc_quant_tensor_fp8.argtypes = [_P, _I32, _I64, _I64, _P, _P]
+        L.orc_quant_tensor_fp8.argtypes = [_P, _I32, _I64, _I64, _P, _P, _I32]
         L.orc_expert_bf16.argtypes = [_P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_expert_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P]
         L.orc_layer_rows.argtypes = [ctypes.POINTER(_Layer), _P, _P, _P, _P, _I32, _P, _I64, _P, _I32]
+        L.orc_layer_rows_trace.argtypes = [ctypes.POINTER(_Layer), _P, _P, _P, _P, _I32, _P, _I64, _P, _I32,
+                                           ctypes.POINTER(_Trace)]
+        L.orc_pt_h.argtypes = [_P, _P, _I64, ctypes.c_double, ctypes.c_double, ctypes.c_double, _P]
         L.orc_combine.argtypes = [_P, _P, _P, _I64, _I32, _I32, _I32, _P]
         L.orc_add_rmsnorm.argtypes = [_P, _P, _P, ctypes.c_double, _I64, _I32, _P, _P]
         _lib = L
@@ -209,7 +216,7 @@ def quant_blocks_fp8(w_bits, nthreads=None):
     return (q[0], s[0]) if squeeze else (q, s)
 
 
-def quant_tensor_fp8(x, mats=1):
+def quant_tensor_fp8(x, mats=1, nthreads=None):
     """Per-tensor FP8 of ``mats`` equal parts of x (bf16 bit patterns as uint16,
     or fp32 values): codes shaped like x and one fp32 scale per part [mats]."""
     f32 = x.dtype == np.float32
@@ -217,8 +224,58 @@ def quant_tensor_fp8(x, mats=1):
     n = x.size // mats
     q = np.empty(x.shape, np.uint8)
     s = np.empty(mats, np.float32)
-    lib().orc_quant_tensor_fp8(_ptr(x), int(f32), mats, n, _ptr(q), _ptr(s))
+    lib().orc_quant_tensor_fp8(_ptr(x), int(f32), mats, n, _ptr(q), _ptr(s), nthreads or default_threads())
     return q, s
+
+
+_E4M3 = None
+
+
+def e4m3_values():
+    """Value of every E4M3 code (float64 [256], NaN for the two NaN codes), from the oracle's codec."""
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = e4m3_value(np.arange(256, dtype=np.uint8))
+    return _E4M3
+
+
+def pt_h_rows(xq, xsc, w1q, s1, w3q, s3):
+    """Per-tensor FP8 h of one expert on the code rows xq [n, H]: fp32 [n, I].
+
+    The code dot products are exact in double in any order of the additions
+    (see ``tensor_dot`` in the C++ file), so they are taken as one float64
+    matrix product of the decoded codes (a library matmul); the scaling, SiLU
+    and the fp32 rounding are the layer's own (``orc_pt_h``)."""
+    dec = e4m3_values()
+    X = dec[_c(xq, np.uint8)]
+    gdot = np.ascontiguousarray(X @ dec[_c(w1q, np.uint8)].T)
+    udot = np.ascontiguousarray(X @ dec[_c(w3q, np.uint8)].T)
+    h = np.empty(gdot.shape, np.float32)
+    lib().orc_pt_h(_ptr(gdot), _ptr(udot), gdot.size, float(xsc), float(s1), float(s3), _ptr(h))
+    return h
+
+
+def pt_h_amax(xq, xsc, ids, E, has_shared, expert):
+    """Per-tensor FP8: the largest |h| over the whole h tensor, i.e. over every
+    (token, expert) pair of every token plus the shared expert's row of every
+    token -- what the h scale amax/448 is taken from.
+
+    xq [T, H] x codes, xsc the x scale, ids [T, k] the routing; expert(g)
+    returns (w1q, s1, w3q, s3) of group g (g == E: the shared expert), so the
+    weights can be streamed one expert at a time."""
+    ids = _c(ids, np.int32)
+    T = ids.shape[0]
+    amax = np.float32(0.0)
+    groups = [(g, np.nonzero((ids == g).any(axis=1))[0]) for g in range(E)]
+    if has_shared:
+        groups.append((E, np.arange(T)))
+    for g, toks in groups:
+        if toks.size == 0:
+            continue
+        w1q, s1, w3q, s3 = expert(g)
+        h = pt_h_rows(xq[toks], xsc, w1q, s1, w3q, s3)
+        amax = max(amax, np.float32(np.abs(h).max()))
+    return float(amax)
 
 
 # ------------------------------------------------------------------ experts / layer
@@ -275,8 +332,13 @@ class Layer:
                                                "sw1", "sw3", "sw2", "ss1", "ss3", "ss2", "h_scale")))
 
 
-def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None):
-    """out[r] = sum_j w[t,j] FFN_{ids[t,j]}(x_t) + FFN_shared(x_t) for t = rows[r] (double)."""
+def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None, trace=False):
+    """out[r] = sum_j w[t,j] FFN_{ids[t,j]}(x_t) + FFN_shared(x_t) for t = rows[r] (double).
+
+    With trace=True returns (out, tr): tr["h"] [nrows, k+S, I] fp32 h of every
+    pair (rank j < k, then the shared expert), and for the FP8 paths
+    tr["hq"] (codes, same shape), tr["hs"] (block FP8: fp32 [nrows, k+S, I/128];
+    MXFP8: E8M0 bytes [nrows, k+S, I/32]) and tr["h_scale"] (per-tensor FP8)."""
     dt = np.uint16 if layer.wtype == 0 else np.uint8
     x = _c(x, dt)
     xs = None if xs is None else _c(xs, np.uint8 if layer.wtype == 2 else np.float32)
@@ -285,9 +347,28 @@ def layer_rows(layer: Layer, x, ids, weights, rows, xs=None, nthreads=None):
     rows = _c(rows, np.int64)
     k = ids.shape[1]
     out = np.empty((rows.size, layer.H), np.float64)
-    lib().orc_layer_rows(ctypes.byref(layer.c), _ptr(x), _ptr(xs), _ptr(ids), _ptr(weights), k,
-                         _ptr(rows), rows.size, _ptr(out), nthreads or default_threads())
-    return out
+    if not trace:
+        lib().orc_layer_rows(ctypes.byref(layer.c), _ptr(x), _ptr(xs), _ptr(ids), _ptr(weights), k,
+                             _ptr(rows), rows.size, _ptr(out), nthreads or default_threads())
+        return out
+    per = k + int(layer.has_shared)
+    I = layer.I
+    tr = {"h": np.empty((rows.size, per, I), np.float32)}
+    hq = hs = hsc = None
+    if layer.wtype != 0:
+        tr["hq"] = hq = np.empty((rows.size, per, I), np.uint8)
+    if layer.wtype == 1:
+        tr["hs"] = hs = np.empty((rows.size, per, I // 128), np.float32)
+    elif layer.wtype == 2:
+        tr["hs"] = hs = np.empty((rows.size, per, I // 32), np.uint8)
+    elif layer.wtype == 3:
+        hsc = np.empty(1, np.float32)
+    c = _Trace(_ptr(tr["h"]), _ptr(hq), _ptr(hs), _ptr(hsc))
+    lib().orc_layer_rows_trace(ctypes.byref(layer.c), _ptr(x), _ptr(xs), _ptr(ids), _ptr(weights), k,
+                               _ptr(rows), rows.size, _ptr(out), nthreads or default_threads(), ctypes.byref(c))
+    if hsc is not None:
+        tr["h_scale"] = float(hsc[0])
+    return out, tr
 
 
 # ------------------------------------------------------------------ combine / norm

@@ -147,3 +147,34 @@ def test_fp8_layer_rows_match_expert_calls(orc):
             e = ids[t, j]
             ref = ref + w[t, j] * orc.expert_fp8(xq[t], xs[t], q1[e], s1[e], q3[e], s3[e], q2[e], s2[e])[1]
         np.testing.assert_allclose(out[t], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_layer_trace_is_the_requantised_h(orc):
+    """The block-FP8 layer's traced h equals the single-expert oracle's fp32 h,
+    and its traced codes and scales are that h quantised per 128 columns (each
+    128-column group as one tensor of the pinned per-tensor quantiser)."""
+    rng = np.random.default_rng(14)
+    T, E, k, H, I = 5, 3, 2, 256, 256
+    w1, w3, w2, sw = _rand_layer(rng, E, H, I, 1, std=0.02)
+    x = torch.from_numpy(rng.standard_normal((T, H))).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xq, xs = orc.quant_rows_fp8(x)
+    q1, s1 = orc.quant_blocks_fp8(w1)
+    q3, s3 = orc.quant_blocks_fp8(w3)
+    q2, s2 = orc.quant_blocks_fp8(w2)
+    qs = [orc.quant_blocks_fp8(a) for a in sw]
+    L = orc.Layer(q1, q3, q2, qs[0][0], qs[1][0], qs[2][0], wtype=1, s1=s1, s3=s3, s2=s2,
+                  ss1=qs[0][1], ss3=qs[1][1], ss2=qs[2][1])
+    ids, w = orc.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    _, tr = orc.layer_rows(L, xq, ids, w, np.arange(T), xs=xs, trace=True)
+    for t in range(T):
+        for j in range(k + 1):
+            if j == k:
+                h = orc.expert_fp8(xq[t], xs[t], qs[0][0], qs[0][1], qs[1][0], qs[1][1], qs[2][0], qs[2][1])[0]
+            else:
+                e = ids[t, j]
+                h = orc.expert_fp8(xq[t], xs[t], q1[e], s1[e], q3[e], s3[e], q2[e], s2[e])[0]
+            np.testing.assert_array_equal(tr["h"][t, j], h.astype(np.float32))
+    groups = tr["h"].reshape(-1, 128)
+    hq, hs = orc.quant_tensor_fp8(groups, mats=groups.shape[0])
+    np.testing.assert_array_equal(tr["hq"].reshape(-1, 128), hq)
+    np.testing.assert_array_equal(tr["hs"].reshape(-1), hs)

@@ -140,3 +140,35 @@ def test_mx_layer_matches_dense_dequantised(orc):
     got = orc.layer_rows(L, xq, ids, wts, rows, xs=xs)
     want = _dense_mx_layer(orc, xq, xs, w1q, w1s, w3q, w3s, w2q, w2s, sw, ids, wts, rows)
     np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12 * np.abs(want).max())
+
+
+def test_mx_layer_trace_is_the_requantised_h(orc):
+    """The layer's traced h equals the dense dequantised h (fp32), and its traced
+    codes and scale bytes are the MX rule applied to that h (quant_rows_mx_f32)."""
+    rng = np.random.default_rng(9)
+    T, H, I, E, k = 6, 256, 256, 3, 2
+    f = lambda *shape, sd: _bf16_bits((rng.standard_normal(shape) * sd).astype(np.float32))
+    xq, xs = orc.quant_rows_mx(f(T, H, sd=1.0))
+    w1q, w1s = orc.quant_rows_mx(f(E, I, H, sd=0.05))
+    w3q, w3s = orc.quant_rows_mx(f(E, I, H, sd=0.05))
+    w2q, w2s = orc.quant_rows_mx(f(E, H, I, sd=0.05))
+    sw = [orc.quant_rows_mx(f(I, H, sd=0.05)), orc.quant_rows_mx(f(I, H, sd=0.05)),
+          orc.quant_rows_mx(f(H, I, sd=0.05))]
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    wts = rng.random((T, k))
+    rows = np.arange(T, dtype=np.int64)
+    L = orc.Layer(w1q, w3q, w2q, sw[0][0], sw[1][0], sw[2][0], wtype=2, s1=w1s, s3=w3s, s2=w2s,
+                  ss1=sw[0][1], ss3=sw[1][1], ss2=sw[2][1])
+    _, tr = orc.layer_rows(L, xq, ids, wts, rows, xs=xs, trace=True)
+    x = _dequant(xq, xs)
+    W1, W3 = _dequant(w1q, w1s), _dequant(w3q, w3s)
+    S1, S3 = _dequant(*sw[0]), _dequant(*sw[1])
+    for t in range(T):
+        for j in range(k + 1):
+            a1, a3 = (S1, S3) if j == k else (W1[ids[t, j]], W3[ids[t, j]])
+            g, u = a1 @ x[t], a3 @ x[t]
+            h = g / (1.0 + np.exp(-g)) * u
+            np.testing.assert_allclose(tr["h"][t, j], h, rtol=2e-7, atol=1e-30)
+    hq, hs = orc.quant_rows_mx_f32(tr["h"])
+    np.testing.assert_array_equal(tr["hq"], hq)
+    np.testing.assert_array_equal(tr["hs"], hs)

@@ -160,3 +160,72 @@ def test_layer_given_h_scale():
     L2 = orc.Layer(q["w1"][0], q["w3"][0], q["w2"][0], q["sw1"][0], q["sw3"][0], q["sw2"][0], h_scale=3 * sh, **kw)
     other = orc.layer_rows(L2, xq, ids, wts, rows, xs=xs)
     assert not np.allclose(other, want[:2], rtol=1e-3)
+
+
+def test_whole_h_amax_closed_form():
+    """The whole-tensor h pass (exact code dot products as one float64 matrix
+    product, then the layer's own scaling) finds the closed-form largest h."""
+    q, xq, xs, ids, wts, want, sh = _closed_form_case()
+    E = q["w1"][0].shape[0]
+
+    def expert(g):
+        if g == E:
+            return q["sw1"][0], q["sw1"][1][0], q["sw3"][0], q["sw3"][1][0]
+        return q["w1"][0][g], q["w1"][1][g], q["w3"][0][g], q["w3"][1][g]
+    amax = orc.pt_h_amax(xq, xs[0], ids, E, True, expert)
+    assert np.float32(amax / np.float32(448.0)) == np.float32(sh)
+
+
+def _random_pt_layer(seed, E=5, H=256, I=256, T=30, k=2):
+    rng = np.random.default_rng(seed)
+    b = {"w1": _rand_bf16((E, I, H), seed + 1, 0.05), "w3": _rand_bf16((E, I, H), seed + 2, 0.05),
+         "w2": _rand_bf16((E, H, I), seed + 3, 0.05), "sw1": _rand_bf16((I, H), seed + 4, 0.05),
+         "sw3": _rand_bf16((I, H), seed + 5, 0.05), "sw2": _rand_bf16((H, I), seed + 6, 0.05)}
+    q = {n: orc.quant_tensor_fp8(b[n], E) for n in ("w1", "w3", "w2")}
+    q.update({n: orc.quant_tensor_fp8(b[n]) for n in ("sw1", "sw3", "sw2")})
+    xq, xs = orc.quant_tensor_fp8(_rand_bf16((T, H), seed + 7))
+    ids, wts = orc.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    return q, xq, xs, ids, wts
+
+
+def test_whole_h_pass_equals_layer_h():
+    """The h of every pair from the whole-tensor pass equals, bit for bit, the
+    h the layer's plain loops compute, and so do the amax and the h scale the
+    layer takes when every token is evaluated."""
+    q, xq, xs, ids, wts = _random_pt_layer(70)
+    E, T, k = q["w1"][0].shape[0], ids.shape[0], ids.shape[1]
+    kw = dict(wtype=3, s1=q["w1"][1], s3=q["w3"][1], s2=q["w2"][1], ss1=q["sw1"][1], ss3=q["sw3"][1],
+              ss2=q["sw2"][1])
+    L = orc.Layer(q["w1"][0], q["w3"][0], q["w2"][0], q["sw1"][0], q["sw3"][0], q["sw2"][0], **kw)
+    rows = np.arange(T)
+    out, tr = orc.layer_rows(L, xq, ids, wts, rows, xs=xs, trace=True)
+    for t in range(T):
+        for j in range(k + 1):
+            g = E if j == k else ids[t, j]
+            w1q, s1 = (q["sw1"][0], q["sw1"][1][0]) if g == E else (q["w1"][0][g], q["w1"][1][g])
+            w3q, s3 = (q["sw3"][0], q["sw3"][1][0]) if g == E else (q["w3"][0][g], q["w3"][1][g])
+            h = orc.pt_h_rows(xq[t:t + 1], xs[0], w1q, s1, w3q, s3)[0]
+            assert np.array_equal(h, tr["h"][t, j]), (t, j)
+
+    def expert(g):
+        if g == E:
+            return q["sw1"][0], q["sw1"][1][0], q["sw3"][0], q["sw3"][1][0]
+        return q["w1"][0][g], q["w1"][1][g], q["w3"][0][g], q["w3"][1][g]
+    amax = orc.pt_h_amax(xq, xs[0], ids, E, True, expert)
+    assert amax == float(np.abs(tr["h"]).max())
+    assert tr["h_scale"] == float(np.float32(np.float32(amax) / np.float32(448.0)))
+    # a subset of the tokens with the whole tensor's scale given is the same rows of the whole
+    sub = np.array([3, 11, 29])
+    L2 = orc.Layer(q["w1"][0], q["w3"][0], q["w2"][0], q["sw1"][0], q["sw3"][0], q["sw2"][0],
+                   h_scale=tr["h_scale"], **kw)
+    assert np.array_equal(orc.layer_rows(L2, xq, ids, wts, sub, xs=xs), out[sub])
+    # h codes of the trace are the quantisation of the trace's h with that scale
+    hq, hs = orc.quant_tensor_fp8(tr["h"])
+    assert np.array_equal(hq, tr["hq"]) and float(hs[0]) == tr["h_scale"]
+
+
+def test_quant_tensor_thread_count_does_not_matter():
+    x = _rand_bf16((3, 300000), 80, 2.0)
+    q1, s1 = orc.quant_tensor_fp8(x, mats=3, nthreads=1)
+    q8, s8 = orc.quant_tensor_fp8(x, mats=3, nthreads=8)
+    assert np.array_equal(q1, q8) and np.array_equal(s1, s8)
