@@ -119,41 +119,118 @@ def load_traffic(name, src_hash):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """CPU model and the host's logical core count, from /proc/cpuinfo and the OS."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+def oracle_threads():
+    """Threads for the oracle: every core this process may run on, at most 16
+    (the GPU machine gives one GPU's job a 16-core share of the host)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
 def cpu_baseline(wl, d, b, budget_s):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload, with all available threads and with one thread.
+
+    Per-step work that depends on all tokens (routing and align, the x
+    quantisation of the FP8 types) runs on every token; the expert FFN and the
+    combine run on the first n tokens (n sized to the time budget), passed
+    over again when one pass is short.  Weight quantisation is offline (done
+    once per model) and not timed.  Per-tensor FP8 takes the h scale from the
+    sampled pairs.  tokens/s = 1 / (FFN+combine time per token + all-token
+    time / T)."""
     from oracle import oracle as orc
-    nthreads = orc.default_threads()
-    x = workloads.bits(d["x"])
-    logits = workloads.bits(d["logits"]) if not wl.router else workloads.bits(b.logits)
-    bias = workloads.bits(d["bias"]) if d["bias"] is not None else None
-    bias_rows = workloads.bits(d["bias_rows"]) if d["bias_rows"] is not None else None
-    if wl.wtype in ("fp8", "mxfp8", "fp8t"):
-        return None
-    L = orc.Layer(*(workloads.bits(d[n]) if d[n] is not None else None
-                    for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2")))
+    nthreads = oracle_threads()
+    model, ncores = host_cpu()
+    host = workloads.bits
+    x = host(d["x"])
+    logits = host(d["logits"]) if not wl.router else host(b.logits)
+    bias = host(d["bias"]) if d["bias"] is not None else None
+    bias_rows = host(d["bias_rows"]) if d["bias_rows"] is not None else None
+
     t0 = time.perf_counter()
     ids, w = orc.route(logits, wl.k, bias, bias_rows)
     orc.align(ids, wl.E, wl.shared)
-    t_route = time.perf_counter() - t0
-    # calibrate on 4 tokens, then size the sample to the time budget
-    rows = np.arange(min(4, wl.T), dtype=np.int64)
-    t0 = time.perf_counter()
-    orc.layer_rows(L, x, ids, w, rows, nthreads=nthreads)
-    per_tok = (time.perf_counter() - t0) / rows.size
-    n = int(max(4, min(wl.T, budget_s / max(per_tok, 1e-9))))
-    # a batch smaller than the budget is passed over again, up to 64 times
-    reps = int(max(1, min(64, budget_s / max(per_tok * n, 1e-9))))
-    rows = np.arange(n, dtype=np.int64)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        orc.layer_rows(L, x, ids, w, rows, nthreads=nthreads)
-    t_ffn = time.perf_counter() - t0
-    per_tok = t_ffn / (n * reps)
-    tok_s = 1.0 / (per_tok + t_route / wl.T)
-    passes = f", {reps} passes" if reps > 1 else ""
-    return {"value": tok_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"route+align on all {wl.T} tokens ({t_route:.3f}s); expert FFN + combine on the first "
-                      f"{n} tokens{passes} ({t_ffn:.2f}s); fp64, {nthreads} threads"}
+    xs = None
+    if wl.wtype == "fp8":
+        x, xs = orc.quant_rows_fp8(x)
+    elif wl.wtype == "mxfp8":
+        x, xs = orc.quant_rows_mx(x, nthreads=nthreads)
+    elif wl.wtype == "fp8t":
+        x, xs = orc.quant_tensor_fp8(x, nthreads=nthreads)
+    t_all = time.perf_counter() - t0
+
+    def layer_for(rows):
+        """Oracle layer over the experts the given tokens use (weights quantised by the oracle, untimed)."""
+        used = np.unique(ids[rows].ravel())
+        remap = np.full(wl.E, -1, np.int32)
+        remap[used] = np.arange(used.size, dtype=np.int32)
+        ids_c = ids.copy()
+        ids_c[rows] = remap[ids[rows]]
+        idx = torch.from_numpy(used).to(d["w1"].device)
+        mats = {n: host(d[n][idx]) for n in ("w1", "w3", "w2")}
+        sh = {n: host(d[n]) if d[n] is not None else None for n in ("sw1", "sw3", "sw2")}
+        if wl.wtype == "bf16":
+            return orc.Layer(mats["w1"], mats["w3"], mats["w2"], sh["sw1"], sh["sw3"], sh["sw2"]), ids_c
+        if wl.wtype == "fp8":
+            qf = lambda a: orc.quant_blocks_fp8(a, nthreads=nthreads)          # noqa: E731
+            wt = 1
+        elif wl.wtype == "mxfp8":
+            qf = lambda a: orc.quant_rows_mx(a, nthreads=nthreads)             # noqa: E731
+            wt = 2
+        else:
+            qf = lambda a: orc.quant_tensor_fp8(a, mats=a.shape[0] if a.ndim == 3 else 1,  # noqa: E731
+                                                nthreads=nthreads)
+            wt = 3
+        q = {n: qf(a) for n, a in mats.items()}
+        qs = {n: (qf(a) if a is not None else (None, None)) for n, a in sh.items()}
+        L = orc.Layer(q["w1"][0], q["w3"][0], q["w2"][0], qs["sw1"][0], qs["sw3"][0], qs["sw2"][0], wtype=wt,
+                      s1=q["w1"][1], s3=q["w3"][1], s2=q["w2"][1], ss1=qs["sw1"][1], ss3=qs["sw3"][1],
+                      ss2=qs["sw2"][1])
+        return L, ids_c
+
+    def timed_pass(threads, budget):
+        # calibrate on 2 tokens, then size the sample to the budget
+        rows = np.arange(min(2, wl.T), dtype=np.int64)
+        L, ids_c = layer_for(rows)
+        t0 = time.perf_counter()
+        orc.layer_rows(L, x, ids_c, w, rows, xs=xs, nthreads=threads)
+        per_tok = (time.perf_counter() - t0) / rows.size
+        n = int(max(2, min(wl.T, budget / max(per_tok, 1e-9))))
+        reps = int(max(1, min(64, budget / max(per_tok * n, 1e-9))))
+        rows = np.arange(n, dtype=np.int64)
+        L, ids_c = layer_for(rows)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            orc.layer_rows(L, x, ids_c, w, rows, xs=xs, nthreads=threads)
+        t = time.perf_counter() - t0
+        return 1.0 / (t / (n * reps) + t_all / wl.T), n, reps, t
+
+    v_n, n_n, r_n, t_n = timed_pass(nthreads, 0.6 * budget_s)
+    v_1, n_1, r_1, t_1 = timed_pass(1, 0.4 * budget_s)
+    prec = "fp64" if wl.wtype == "bf16" else "fp64 with the FP8 quantisation emulated exactly"
+    return {"value": v_n, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "value_1thread": v_1, "host_cores": ncores, "cpu_model": model,
+            "sample": f"per-step work over all {wl.T} tokens (route+align"
+                      f"{', x quantisation' if wl.wtype != 'bf16' else ''}: {t_all:.2f}s); expert FFN + combine "
+                      f"on the first {n_n} tokens x {r_n} passes ({t_n:.1f}s, {nthreads} threads) and the first "
+                      f"{n_1} tokens x {r_1} passes ({t_1:.1f}s, 1 thread); {prec}"
+                      + ("; h scale from the sampled pairs" if wl.wtype == "fp8t" else "")}
 
 
 def main():
@@ -212,11 +289,6 @@ def main():
         g = torch.Generator(device=dev).manual_seed(wl.seed + 17)
         kw["residual"] = torch.randn((wl.T, wl.H), generator=g, device=dev).to(torch.bfloat16)
         kw["norm_weight"] = (1.0 + 0.1 * torch.randn(wl.H, generator=g, device=dev)).to(torch.bfloat16)
-    if fp8:   # fp8 weights are quantised once; the bf16 copies are not needed any more
-        for n in ("w1", "w3", "w2", "sw1", "sw3", "sw2"):
-            d[n] = None
-        torch.cuda.empty_cache()
-
     stream = torch.cuda.current_stream()
     names = (["router"] if wl.router else []) + ["route", "align"] + (["quant"] if fp8 else []) + \
         ["gemm13"] + (["hquant"] if wl.wtype == "fp8t" else []) + ["gemm2", "combine"]
@@ -306,6 +378,10 @@ def main():
         achieved = g13_flops / g13_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": load_traffic(wl.name, src_hash)}
+    if roof["traffic"] is not None:
+        roof["traffic_source"] = (f"profiles/gemm13_{wl.name}_traffic.json: rocprofv3 FETCH_SIZE + WRITE_SIZE of "
+                                  "this kernel, calibrated on a device copy, taken on these kernel sources "
+                                  "(not measured in this run)")
     roof["kernel"] = "gemm13"
     roof["per_launch"] = {"bytes": g13_bytes, "flops": g13_flops, "touched_experts": touched,
                           "avg_ms": stage_ms["gemm13"]}
