@@ -113,6 +113,24 @@ GemmArgs gemm_args(const moe_experts_t* ex, int64_t T, int k, const int32_t* off
   return a;
 }
 
+// A persistent chain only completes when every workgroup of its grid is
+// resident at once (its waves wait on items that other waves of the same grid
+// hold).  Two chains running side by side on one device could each get only
+// part of the device and then wait until their waits expire, so the library
+// orders its own chains per device: each call's stream waits for the previous
+// call's completion event before the chain is enqueued.  Inside a stream
+// capture the graph's own ordering applies instead (events from outside a
+// capture cannot be waited on there).
+constexpr int kMaxDevices = 64;
+struct ChainOrder {
+  std::mutex m;
+  hipEvent_t last[kMaxDevices] = {};
+};
+ChainOrder& chain_order() {
+  static ChainOrder o;
+  return o;
+}
+
 }  // namespace
 
 #define MOE_GUARD_BEGIN try {
@@ -507,22 +525,12 @@ int check_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void*
   return MOE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, void* stream) {
-  MOE_GUARD_BEGIN
-  FwdLayout L;
-  bool empty;
-  const int st = check_forward(ex, args, ws, ws_bytes, &L, &empty);
-  if (st != MOE_OK || empty) return st;
+// Enqueue the whole chain with its intermediates laid out at `base` (already validated).
+int forward_enqueue(const moe_experts_t* ex, const moe_forward_args_t* args, char* base, const FwdLayout& L,
+                    hipStream_t s) {
   const int64_t T = args->T;
   const int k = args->k;
   const bool router = args->logits == nullptr;
-
-  char* base = static_cast<char*>(ws);
-  hipStream_t s = (hipStream_t)stream;
   const int E = ex->E;
   const bool mx = ex->wtype == MOE_W_MXFP8;
   const bool pt = ex->wtype == MOE_W_FP8_TENSOR;
@@ -589,6 +597,19 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   if (e != hipSuccess) return MOE_EDEVICE;
   e = launch_combine(y, args->y_dtype, pair_slot, w, T, k, ex->H, ex->has_shared, args->out, s);
   return device_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, void* stream) {
+  MOE_GUARD_BEGIN
+  FwdLayout L;
+  bool empty;
+  const int st = check_forward(ex, args, ws, ws_bytes, &L, &empty);
+  if (st != MOE_OK || empty) return st;
+  return forward_enqueue(ex, args, static_cast<char*>(ws), L, (hipStream_t)stream);
   MOE_GUARD_END
 }
 
@@ -614,6 +635,22 @@ int moe_forward_persistent(const moe_experts_t* ex, const moe_forward_args_t* ar
     const hipError_t e = launch_router_gemm(args->x, args->router_hi, args->router_lo, logits, T, ex->H, ex->E, s);
     if (e != hipSuccess) return MOE_EDEVICE;
   }
+  // (the router GEMM above is an ordinary kernel; only the chain needs the device to itself)
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return MOE_EDEVICE;
+  int dev = 0;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  ChainOrder& order = chain_order();
+  std::lock_guard<std::mutex> lock(order.m);
+  const bool ordered = cap == hipStreamCaptureStatusNone;
+  if (ordered) {
+    if (order.last[dev] == nullptr &&
+        hipEventCreateWithFlags(&order.last[dev], hipEventDisableTiming) != hipSuccess) {
+      order.last[dev] = nullptr;
+      return MOE_EDEVICE;
+    }
+    if (hipStreamWaitEvent(s, order.last[dev], 0) != hipSuccess) return MOE_EDEVICE;
+  }
   ChainBuffers b;
   b.logits = router ? logits : args->logits;
   b.bias = args->bias;
@@ -630,7 +667,10 @@ int moe_forward_persistent(const moe_experts_t* ex, const moe_forward_args_t* ar
   b.y_dtype = args->y_dtype;
   b.out = args->out;
   b.ctl = reinterpret_cast<int*>(base + L.ctl);
-  return device_status(launch_chain(a, b, s));
+  const hipError_t e = launch_chain(a, b, s);
+  if (e != hipSuccess) return MOE_EDEVICE;
+  if (ordered && hipEventRecord(order.last[dev], s) != hipSuccess) return MOE_EDEVICE;
+  return MOE_OK;
   MOE_GUARD_END
 }
 

@@ -304,7 +304,20 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
  * chain kernel ([router_gemm] first when logits is NULL).
  * Envelope: wtype MOE_W_BF16 and at most 16 routed rows per expert on average
  * (T*k <= 16*E); anything else returns MOE_EUNSUPPORTED with nothing enqueued.
- * Two calls that share a workspace must not run concurrently.
+ *
+ * Residency: the chain kernel's grid is sized to what the device holds at
+ * once, and it completes only if all of its workgroups are resident together
+ * (waves wait on items that other waves of the grid hold).  The caller must
+ * therefore not run other kernels on the device while the chain runs.  The
+ * library orders its own chains: on each device, every call's stream first
+ * waits for the previous call's chain (an event the library keeps), so chains
+ * on different streams never overlap.  Calls made during a stream capture are
+ * not ordered this way (the captured graph's own order applies); the caller
+ * must not replay such a graph beside another chain.  If the device is
+ * shared anyway, every device-side wait ends after about 0.67 s: the call has
+ * already returned MOE_OK, out is undefined, and moe_forward_persistent_status
+ * reports MOE_EDEVICE.  Two calls that share a workspace must not run
+ * concurrently.
  */
 int moe_forward_persistent(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes,
                            void* stream);

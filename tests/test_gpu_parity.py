@@ -52,6 +52,8 @@ SMALL = [
     # 224 to 288 rows per expert on average: 288-row tiles, with remainders
     # where the Zipf-biased experts overflow them
     W("tall-tiles", T=500, H=256, E=16, k=8, I=128, shared=1, bias="mix", bias_frac=0.3, seed=38),
+    # Zipf ranks permuted: the hot experts sit at scattered indices, some late in the item order
+    W("zipf-perm", T=500, H=256, E=32, k=8, I=128, shared=1, bias="all", bias_perm=5, seed=39),
 ]
 
 
@@ -65,6 +67,7 @@ FP8_SMALL = [
     W("fp8-medium", T=300, H=512, E=16, k=4, I=256, shared=1, wtype="fp8", seed=21),
     W("fp8-ragged", T=37, H=384, E=8, k=3, I=384, shared=0, wtype="fp8", seed=22),
     W("fp8-zipf", T=400, H=256, E=32, k=8, I=256, shared=1, wtype="fp8", bias="all", seed=23),
+    W("fp8-zipf-perm", T=500, H=256, E=32, k=8, I=256, shared=1, wtype="fp8", bias="all", bias_perm=6, seed=28),
 ]
 
 

@@ -165,3 +165,30 @@ RANDOM = _random_shapes(16, 2025)
 @pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
 def test_persistent_random_shapes(wl):
     test_persistent_matches_chain_and_oracle(wl, moe.MOE_DTYPE_F32 if wl.T % 2 else moe.MOE_DTYPE_BF16)
+
+
+def test_persistent_chains_on_two_streams():
+    """Two persistent chains enqueued on two streams at once: the library orders
+    them on the device, so both complete (status OK) with their serial bits."""
+    shapes = [W("pc-a", T=64, H=1024, E=64, k=8, I=256, shared=1, seed=91),
+              W("pc-b", T=48, H=512, E=32, k=4, I=384, shared=1, bias="mix", bias_frac=0.3, seed=92)]
+    runs = []
+    for wl in shapes:
+        log(f"two-stream persistent {wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I}")
+        d = workloads.make_inputs(wl, device="cuda")
+        layer = _layer(d)
+        want, _, _, ws = _forward(moe.moe_forward_persistent, layer, wl, d, moe.MOE_DTYPE_F32)
+        moe.moe_forward_persistent_status(ws)
+        runs.append((wl, layer, d, ws, torch.empty_like(want), want))
+    streams = [torch.cuda.Stream() for _ in runs]
+    for rep in range(3):
+        for s, (wl, layer, d, ws, out, _) in zip(streams, runs):
+            out.zero_()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                moe.moe_forward_persistent(layer.experts, d["x"], wl.k, out, ws, logits=d["logits"], bias=d["bias"],
+                                           bias_rows=d["bias_rows"], y_dtype=moe.MOE_DTYPE_F32)
+        torch.cuda.synchronize()
+        for (wl, _, _, ws, out, want) in runs:
+            moe.moe_forward_persistent_status(ws)
+            assert torch.equal(out, want), f"{wl.name}, repeat {rep}"

@@ -16,10 +16,14 @@ Workloads (shapes and distributions of the five layer configurations):
            expert matrix, per x, per h)
   router   T=16384 H=6144 E=256 k=8 I=2048 + shared expert, bf16, fp32 router
            weights [E,H], 30% of tokens carry the Zipf logit bias
+  fp8perm  the fp8 workload with the Zipf ranks permuted (seeded), so the hot
+           experts sit at scattered expert indices instead of 0, 1, 2, ...
 Distributions: weights bf16 ~N(0, 0.02), activations bf16 ~N(0, 1), router
 logits fp32 ~N(0, 1), router weights fp32 ~N(0, 0.01).  Values are drawn in
 fp32 and rounded to bf16 by torch's round-to-nearest-even conversion.  The
-Zipf bias is b_e = 2 ln(1 / (e + 1)), i.e. rank(e) = e + 1.
+Zipf bias is b_e = 2 ln(1 / rank(e)) with rank(e) = e + 1, or with
+rank(e) = perm[e] + 1 for a seeded permutation perm of [0, E) when the
+workload sets bias_perm.
 """
 from __future__ import annotations
 
@@ -43,6 +47,7 @@ class Workload:
     bias: str = "none"           # "none", "all" (every row biased) or "mix"
     bias_frac: float = 0.0       # fraction of biased rows for "mix"
     router: bool = False         # logits come from the split-bf16 router GEMM
+    bias_perm: int = 0           # nonzero: seed of a permutation of the Zipf ranks
     seed: int = 0
     w_std: float = 0.02
     x_std: float = 1.0
@@ -70,6 +75,8 @@ WORKLOADS = {
                      bias="all", seed=1007),
     "router": Workload("router", T=16384, H=6144, E=256, k=8, I=2048, shared=1, bias="mix",
                        bias_frac=0.3, router=True, seed=1005),
+    "fp8perm": Workload("fp8perm", T=4096, H=6144, E=256, k=8, I=2048, shared=1, wtype="fp8",
+                        bias="all", bias_perm=77, seed=1004),
 }
 
 
@@ -77,9 +84,13 @@ def workload(name: str, **overrides) -> Workload:
     return replace(WORKLOADS[name], **overrides)
 
 
-def zipf_bias(E: int) -> np.ndarray:
-    """b_e = 2 ln(1/(e+1)) as fp32 (expert 0 is the hottest)."""
-    return np.array([2.0 * math.log(1.0 / (e + 1)) for e in range(E)], dtype=np.float32)
+def zipf_bias(E: int, perm_seed: int = 0) -> np.ndarray:
+    """b_e = 2 ln(1/rank(e)) as fp32: rank(e) = e + 1 (expert 0 is the hottest),
+    or perm[e] + 1 for a permutation of [0, E) drawn from perm_seed."""
+    rank = np.arange(E) + 1
+    if perm_seed:
+        rank = np.random.default_rng(perm_seed).permutation(E) + 1
+    return np.array([2.0 * math.log(1.0 / int(r)) for r in rank], dtype=np.float32)
 
 
 def _normal(shape, std, gen, device, dtype):
@@ -109,7 +120,7 @@ def make_inputs(wl: Workload, device="cpu", seed: int | None = None, weights: bo
     d["bias"] = None
     d["bias_rows"] = None
     if wl.bias in ("all", "mix"):
-        d["bias"] = torch.from_numpy(zipf_bias(E)).to(device)
+        d["bias"] = torch.from_numpy(zipf_bias(E, wl.bias_perm)).to(device)
     if wl.bias == "mix":
         cpu_gen = torch.Generator()
         cpu_gen.manual_seed(seed + 1)
