@@ -68,6 +68,7 @@ _SIGS = {
     "moe_forward": (_I32, [ctypes.POINTER(moe_experts_t), ctypes.POINTER(moe_forward_args_t), _P, _SZ, _P]),
     "moe_forward_persistent": (_I32, [ctypes.POINTER(moe_experts_t), ctypes.POINTER(moe_forward_args_t), _P, _SZ,
                                       _P]),
+    "moe_forward_noalloc": (_I32, [ctypes.POINTER(moe_experts_t), ctypes.POINTER(moe_forward_args_t), _P]),
     "moe_forward_persistent_status": (_I32, [_P, _P]),
 }
 
@@ -298,6 +299,18 @@ def moe_forward(ex: Experts, x, k, out, ws, logits=None, router_hi=None, router_
                               _ptr(bias_rows), _ptr(out), _ptr(topk_ids), _ptr(topk_w))
     nbytes = ws.numel() * ws.element_size()
     _check(lib().moe_forward(ex.ref, ctypes.byref(args), _ptr(ws), nbytes, _stream(x)), "moe_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(ex: Experts, x, k, out, logits=None, router_hi=None, router_lo=None, bias=None,
+                        bias_rows=None, y_dtype=MOE_DTYPE_F32, topk_ids=None, topk_w=None):
+    """moe_forward with its intermediates in the library's fixed device scratch (no workspace)."""
+    T = x.shape[0]
+    args = moe_forward_args_t(T, k, y_dtype, _ptr(x), _ptr(logits), _ptr(router_hi), _ptr(router_lo), _ptr(bias),
+                              _ptr(bias_rows), _ptr(out), _ptr(topk_ids), _ptr(topk_w))
+    _check(lib().moe_forward_noalloc(ex.ref, ctypes.byref(args), _stream(x)), "moe_forward_noalloc")
 
 
 def moe_forward_persistent(ex: Experts, x, k, out, ws, logits=None, router_hi=None, router_lo=None, bias=None,

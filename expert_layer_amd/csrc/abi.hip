@@ -494,10 +494,13 @@ size_t moe_forward_workspace_bytes(const moe_experts_t* ex, int64_t T, int k, in
 
 namespace {
 
-// Argument checks shared by moe_forward and moe_forward_persistent.  On
-// MOE_OK with T > 0, *L is the workspace layout.
+// Argument checks shared by moe_forward, moe_forward_persistent and
+// moe_forward_noalloc.  On MOE_OK with T > 0, *L is the workspace layout.
+// With fixed_scratch the workspace is the library's own scratch array (ws is
+// ignored): the layout must fit in MOE_NOALLOC_SCRATCH_BYTES, else
+// MOE_EUNSUPPORTED.
 int check_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes, FwdLayout* L,
-                  bool* empty) {
+                  bool* empty, bool fixed_scratch = false) {
   *empty = false;
   if (!args) return MOE_EINVAL;
   int st = check_experts(ex);
@@ -519,6 +522,7 @@ int check_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void*
   if (router && (!aligned16(args->router_hi) || !aligned16(args->router_lo))) return MOE_EINVAL;
   // the workspace always has room for the logits, matching moe_forward_workspace_bytes
   *L = forward_layout(ex, T, k, args->y_dtype, true);
+  if (fixed_scratch) return L->total <= MOE_NOALLOC_SCRATCH_BYTES ? MOE_OK : MOE_EUNSUPPORTED;
   if (ws == nullptr || ws_bytes < L->total) return MOE_EWORKSPACE;
   if (overlap(ws, L->total, args->out, (size_t)T * ex->H * 2) || overlap(ws, L->total, args->x, (size_t)T * ex->H * 2))
     return MOE_EINVAL;
@@ -599,6 +603,35 @@ int forward_enqueue(const moe_experts_t* ex, const moe_forward_args_t* args, cha
   return device_status(e);
 }
 
+// Device scratch of moe_forward_noalloc: the chain's intermediates for callers
+// that cannot allocate.  Each device the library runs on holds its own copy
+// until the process ends.  In host code this name is only a handle for
+// hipGetSymbolAddress; kernels get the device address scratch_address returns.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddrs {
+  std::mutex m;
+  void* ptr[kMaxDevices] = {};
+};
+
+// Device address of `scratch` on device dev, looked up once per device with
+// that device current; nullptr if the lookup fails.
+void* scratch_address(int dev) {
+  static ScratchAddrs addrs;
+  std::lock_guard<std::mutex> lock(addrs.m);
+  if (addrs.ptr[dev] == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess) return nullptr;
+    addrs.ptr[dev] = p;
+  }
+  return addrs.ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -610,6 +643,21 @@ int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* w
   const int st = check_forward(ex, args, ws, ws_bytes, &L, &empty);
   if (st != MOE_OK || empty) return st;
   return forward_enqueue(ex, args, static_cast<char*>(ws), L, (hipStream_t)stream);
+  MOE_GUARD_END
+}
+
+int moe_forward_noalloc(const moe_experts_t* ex, const moe_forward_args_t* args, void* stream) {
+  MOE_GUARD_BEGIN
+  FwdLayout L;
+  bool empty;
+  const int st = check_forward(ex, args, nullptr, 0, &L, &empty, true);
+  if (st != MOE_OK || empty) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  void* base = scratch_address(dev);
+  if (base == nullptr) return MOE_EDEVICE;
+  return forward_enqueue(ex, args, static_cast<char*>(base), L, s);
   MOE_GUARD_END
 }
 

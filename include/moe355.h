@@ -292,6 +292,23 @@ size_t moe_forward_workspace_bytes(const moe_experts_t* ex, int64_t T, int k, in
 int moe_forward(const moe_experts_t* ex, const moe_forward_args_t* args, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* ------------------------------------------------------------------ the chain without a workspace
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): moe_forward
+ * with every intermediate in a fixed device scratch array the library owns,
+ * MOE_NOALLOC_SCRATCH_BYTES on each device it runs on (held until the process
+ * ends).  The caller passes inputs and outputs only; the call allocates
+ * nothing.  Same arguments (minus the workspace), checks, kernels and result
+ * bits as moe_forward.  A shape whose moe_forward_workspace_bytes exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES returns MOE_EUNSUPPORTED with nothing enqueued
+ * (e.g. decode-sized batches of 64 tokens at H = 6144 fit; prefill batches do
+ * not).  Every call on a device uses that device's one scratch array: calls
+ * that overlap on one device (other streams, other threads) race and give
+ * undefined results; the caller must order them.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_experts_t* ex, const moe_forward_args_t* args, void* stream);
+
 /* ------------------------------------------------------------------ the chain in one launch
  * Same arguments, workspace and result as moe_forward, bitwise: the stages run
  * as phases of one persistent kernel that hands out work items in chain order

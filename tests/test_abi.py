@@ -34,7 +34,7 @@ def L():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert sorted(moe.exported_symbols()) == names
@@ -180,6 +180,25 @@ def test_forward_validation(L):
     assert L.moe_forward(ctypes.byref(ex), None, ws, need, None) == moe.MOE_EINVAL
     args0 = moe.moe_forward_args_t(0, 2, 0, None, B, None, None, None, None, None, None, None)
     assert L.moe_forward(ctypes.byref(ex), ctypes.byref(args0), None, 0, None) == moe.MOE_OK
+
+
+def test_forward_noalloc_validation(L):
+    """Host-only checks of the workspace-free chain: argument errors as for
+    moe_forward, and shapes whose intermediates exceed the fixed scratch are
+    refused with MOE_EUNSUPPORTED before anything touches the device."""
+    fn = L.moe_forward_noalloc
+    ex = _experts(has_shared=0)
+    args2 = moe.moe_forward_args_t(16, 2, 0, A, None, None, None, None, None, C, None, None)
+    assert fn(ctypes.byref(ex), ctypes.byref(args2), None) == moe.MOE_EINVAL   # no logits, no router
+    args3 = moe.moe_forward_args_t(16, 2, 5, A, B, None, None, None, None, C, None, None)
+    assert fn(ctypes.byref(ex), ctypes.byref(args3), None) == moe.MOE_EUNSUPPORTED
+    assert fn(ctypes.byref(ex), None, None) == moe.MOE_EINVAL
+    big_T = 1 << 16
+    assert L.moe_forward_workspace_bytes(ctypes.byref(ex), big_T, 2, 0) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    big = moe.moe_forward_args_t(big_T, 2, 0, A, B, None, None, None, None, C, None, None)
+    assert fn(ctypes.byref(ex), ctypes.byref(big), None) == moe.MOE_EUNSUPPORTED
+    args0 = moe.moe_forward_args_t(0, 2, 0, None, B, None, None, None, None, None, None, None)
+    assert fn(ctypes.byref(ex), ctypes.byref(args0), None) == moe.MOE_OK
 
 
 def test_forward_persistent_validation(L):
