@@ -51,6 +51,12 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host stub the compiler silently dropped links fine into a
+    # shared library and only fails when it is loaded: refuse such a build
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.strip() for ln in nm.stdout.splitlines() if "moe355::" in ln]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError("link left library symbols undefined:\n" + "\n".join(missing or [nm.stderr]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
