@@ -152,6 +152,15 @@ hipError_t launch_gemm13_pt(const GemmArgs& a, const uint8_t* xq, const float* x
 hipError_t launch_gemm2_pt(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
                            hipStream_t s);
 
+// weight-streaming MXFP8 / per-tensor kernels for small groups (pt: per-tensor
+// Down, hs then holds the fp32 h scale)
+hipError_t launch_gemm13_mx_stream(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq,
+                                   uint8_t* hs, hipStream_t s);
+hipError_t launch_gemm13_pt_stream(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
+                                   hipStream_t s);
+hipError_t launch_gemm2_mx_stream(const GemmArgs& a, const uint8_t* hq, const uint8_t* hs, void* y, int y_dtype,
+                                  int pt, hipStream_t s);
+
 bool tiled_fp8_gemm13_ok(const GemmArgs& a);
 bool tiled_fp8_gemm2_ok(const GemmArgs& a);
 hipError_t launch_gemm13_fp8_tiled(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq, float* hs,

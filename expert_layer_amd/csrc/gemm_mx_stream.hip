@@ -1,0 +1,286 @@
+// Weight-streaming grouped GEMMs for MXFP8 and per-tensor FP8 experts with
+// small groups (decode-shaped batches: up to 16 rows per expert on average),
+// where the tiled kernels would run mostly padded 256-row tiles.
+//
+// MXFP8 is the microscaling FP8 format the PR #54160 report lists beside the
+// FP8 blockwise 128x128 scales (implementation item 4); per-tensor FP8 is the
+// second mode of the HPC-Ops page's FP8 GroupGEMM (main functions).  Both run
+// on v_mfma_scale_f32_16x16x128_f8f6f4: lane (r, j) of a 16-row fragment holds
+// K bytes 16 j .. +15 and 64 + 16 j .. +15 of row r's 128-byte K block and
+// supplies the E8M0 scale of that row's j-th 32-value block, so the matrix
+// core applies every MX block scale itself and the block products accumulate
+// in place.  Per-tensor mode passes unit scales and scales the whole-K sums
+// once in the epilogue (activation scale x the expert matrix's scale).
+//
+// An item is a 16-row chunk of one group (the chunk table of tiles.hpp) and a
+// slab of weight rows; every weight row of the slab is read once per chunk,
+// which for these batches means once.  kD K blocks of each operand (codes and
+// MX scale bytes) are in flight per wave.  Rows past the chunk's end read nothing (zeros), and their
+// results are not stored.
+//   * Gate-Up: a workgroup of 4 waves owns one chunk x 128 h columns; wave w
+//     owns columns 32 w .. +31 (gate and up rows), which for MX are exactly
+//     one 32-column block of the requantised h, so the row amax is a 16-lane
+//     shuffle (the layout of the tiled MX epilogue).  Per-tensor writes h in
+//     fp32 and folds max |h| into one word with an integer atomicMax on the
+//     float's bits (non-negative floats order like their bit patterns).
+//   * Down: a wave owns one chunk x 16 output columns over the whole K = I.
+// The A rows of the Gate-Up are gathered from x through the routing index.
+#include "tiles.hpp"
+
+namespace moe355 {
+
+namespace {
+
+constexpr int kD = 2;          // K blocks of 128 in flight per wave
+constexpr int kWaves13 = 4;    // Gate-Up workgroup: 4 waves x 32 columns
+
+__device__ __forceinline__ i32x8_t ld_frag(const uint8_t* p) {
+  // the two 16-byte pieces of a lane: bytes 0..15 and 64..79 from p
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p);
+  const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(p + 64);
+  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// block-scaled MFMA, E4M3 operands (format 0), scales in byte 0 of sa / sb
+__device__ __forceinline__ f32x4_t mfma_mx(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// this lane's E8M0 byte (block lq of K block kb) from a row of scale bytes
+// [K / 32]; 127 (2^0) for a row that is not there
+__device__ __forceinline__ int scale_byte(const uint8_t* row, int kb, int lq) {
+  return row ? (int)row[4 * kb + lq] : 127;
+}
+
+// ---------------------------------------------------------------- Gate-Up
+template <int PT>
+__global__ __launch_bounds__(64 * kWaves13) void gemm13_mx_stream(GemmArgs a, const uint8_t* __restrict__ xq,
+                                                                  const uint8_t* __restrict__ xs,
+                                                                  void* __restrict__ hout,
+                                                                  uint8_t* __restrict__ hs) {
+  __shared__ ChunkTable tab;
+  const int G = a.E + (a.has_shared ? 1 : 0);
+  const int nchunks = build_chunks(tab, a.offsets, G, 16);
+  const int H = a.H, I = a.I;
+  const int KB = H / 128, NB = I / 128, HM = H / 32;
+  const int64_t items = (int64_t)nchunks * NB;
+  const int64_t P = a.T * a.k;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const i32x8_t zero = {};
+  float hmax = 0.0f;   // per-tensor: running max |h| of this thread
+
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int c = (int)(it / NB);
+    const int nb = (int)(it % NB);
+    const int n0 = nb * 128 + wave * 32;
+    const int g = chunk_group(tab, G, c);
+    const int r0 = a.offsets[g] + (c - tab.prefix[g]) * 16;
+    const int rend = min(r0 + 16, a.offsets[g + 1]);
+    const bool shared = g == a.E;
+    const int64_t mat = (int64_t)I * H;
+    const uint8_t* w1 = shared ? static_cast<const uint8_t*>(a.sw1) : static_cast<const uint8_t*>(a.w1) + g * mat;
+    const uint8_t* w3 = shared ? static_cast<const uint8_t*>(a.sw3) : static_cast<const uint8_t*>(a.w3) + g * mat;
+    // B rows: f = 0, 1 gate rows n0 + 16 f + lr, f = 2, 3 the matching up rows
+    const uint8_t* bp[4];
+    const uint8_t* bs[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int row = n0 + 16 * (f & 1) + lr;
+      bp[f] = (f < 2 ? w1 : w3) + (int64_t)row * H + 16 * lq;
+      if (PT) {
+        bs[f] = nullptr;
+      } else {
+        const uint8_t* sm = reinterpret_cast<const uint8_t*>(f < 2 ? (shared ? a.ss1 : a.s1) : (shared ? a.ss3 : a.s3));
+        bs[f] = sm + ((shared ? 0 : (int64_t)g * I) + row) * HM;
+      }
+    }
+    // A: row r0 + lr (token gathered through the routing index)
+    const int ra = r0 + lr;
+    const uint8_t* ap = nullptr;
+    const uint8_t* as = nullptr;
+    if (ra < rend) {
+      const int64_t t = ra < P ? (int64_t)(a.slot_pair[ra] / a.k) : (int64_t)ra - P;
+      ap = xq + t * H + 16 * lq;
+      if (!PT) as = xs + t * HM;
+    }
+    f32x4_t acc[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // codes and scale bytes of kD K blocks in flight (the scales travel with
+    // their codes, so their latency is hidden as well)
+    i32x8_t av[kD], bv[kD][4];
+    int sav[kD], sbv[kD][4];
+    auto load = [&](int s, int kb) {
+      av[s] = ap ? ld_frag(ap + 128 * kb) : zero;
+      sav[s] = PT ? 127 : scale_byte(as, kb, lq);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        bv[s][f] = ld_frag(bp[f] + 128 * kb);
+        sbv[s][f] = PT ? 127 : scale_byte(bs[f], kb, lq);
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < kD; ++s)
+      if (s < KB) load(s, s);
+    for (int kb0 = 0; kb0 < KB; kb0 += kD) {
+#pragma unroll
+      for (int s = 0; s < kD; ++s) {
+        const int kb = kb0 + s;
+        if (kb < KB) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[f] = mfma_mx(av[s], bv[s][f], acc[f], sav[s], sbv[s][f]);
+          if (kb + kD < KB) load(s, kb + kD);
+        }
+      }
+    }
+    // lane (lr, lq) holds rows 4 lq + i, columns lr (f = 0 / 2) and lr + 16 (f = 1 / 3)
+    if (PT) {
+      const float xsc = reinterpret_cast<const float*>(xs)[0];
+      const float gs = xsc * (shared ? a.ss1[0] : a.s1[g]);
+      const float us = xsc * (shared ? a.ss3[0] : a.s3[g]);
+      float* hf = static_cast<float*>(hout);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * lq + i;
+        if (r < rend) {
+          const float h0 = silu_mul(acc[0][i] * gs, acc[2][i] * us);
+          const float h1 = silu_mul(acc[1][i] * gs, acc[3][i] * us);
+          hf[(int64_t)r * I + n0 + lr] = h0;
+          hf[(int64_t)r * I + n0 + 16 + lr] = h1;
+          hmax = fmaxf(hmax, fmaxf(fabsf(h0), fabsf(h1)));
+        }
+      }
+    } else {
+      uint8_t* hq = static_cast<uint8_t*>(hout);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float h0 = silu_mul(acc[0][i], acc[2][i]);
+        const float h1 = silu_mul(acc[1][i], acc[3][i]);
+        const int X = mx_exponent(wave_max16(fmaxf(fabsf(h0), fabsf(h1))));
+        const uint32_t codes = f32x2_to_e4m3(ldexp_f32(h0, -X), ldexp_f32(h1, -X));
+        const int r = r0 + 4 * lq + i;
+        if (r < rend) {
+          hq[(int64_t)r * I + n0 + lr] = (uint8_t)(codes & 0xFF);
+          hq[(int64_t)r * I + n0 + 16 + lr] = (uint8_t)(codes >> 8);
+          if (lr == 0) hs[(int64_t)r * (I / 32) + (n0 >> 5)] = (uint8_t)(X + 127);
+        }
+      }
+    }
+  }
+  if (PT) {
+    __shared__ float red[kWaves13];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+    if (lane == 0) red[wave] = hmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mx = red[0];
+      for (int w = 1; w < kWaves13; ++w) mx = fmaxf(mx, red[w]);
+      if (mx > 0.0f) atomicMax(reinterpret_cast<unsigned*>(hs), __float_as_uint(mx));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- Down
+template <int PT, int YBF16>
+__global__ __launch_bounds__(256) void gemm2_mx_stream(GemmArgs a, const uint8_t* __restrict__ hq,
+                                                       const uint8_t* __restrict__ hs, void* __restrict__ y) {
+  __shared__ ChunkTable tab;
+  const int G = a.E + (a.has_shared ? 1 : 0);
+  const int nchunks = build_chunks(tab, a.offsets, G, 16);
+  const int H = a.H, I = a.I;
+  const int KB = I / 128, IM = I / 32;
+  const int NT = H / 16;
+  const int64_t items = (int64_t)nchunks * NT;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const i32x8_t zero = {};
+
+  for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items; it += nwaves) {
+    const int c = (int)(it / NT);
+    const int n0 = (int)(it % NT) * 16;
+    const int g = chunk_group(tab, G, c);
+    const int r0 = a.offsets[g] + (c - tab.prefix[g]) * 16;
+    const int rend = min(r0 + 16, a.offsets[g + 1]);
+    const bool shared = g == a.E;
+    const int64_t mat = (int64_t)I * H;
+    const uint8_t* w2 = shared ? static_cast<const uint8_t*>(a.sw2) : static_cast<const uint8_t*>(a.w2) + g * mat;
+    const uint8_t* bp = w2 + (int64_t)(n0 + lr) * I + 16 * lq;
+    const uint8_t* bs = nullptr;
+    if (!PT) {
+      const uint8_t* sm = reinterpret_cast<const uint8_t*>(shared ? a.ss2 : a.s2);
+      bs = sm + ((shared ? 0 : (int64_t)g * H) + n0 + lr) * IM;
+    }
+    const int ra = r0 + lr;
+    const uint8_t* ap = ra < rend ? hq + (int64_t)ra * I + 16 * lq : nullptr;
+    const uint8_t* as = (!PT && ra < rend) ? hs + (int64_t)ra * IM : nullptr;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    i32x8_t av[kD], bw[kD];
+    int sav[kD], sbv[kD];
+    auto load = [&](int s, int kb) {
+      av[s] = ap ? ld_frag(ap + 128 * kb) : zero;
+      bw[s] = ld_frag(bp + 128 * kb);
+      sav[s] = PT ? 127 : scale_byte(as, kb, lq);
+      sbv[s] = PT ? 127 : scale_byte(bs, kb, lq);
+    };
+#pragma unroll
+    for (int s = 0; s < kD; ++s)
+      if (s < KB) load(s, s);
+    for (int kb0 = 0; kb0 < KB; kb0 += kD) {
+#pragma unroll
+      for (int s = 0; s < kD; ++s) {
+        const int kb = kb0 + s;
+        if (kb < KB) {
+          acc = mfma_mx(av[s], bw[s], acc, sav[s], sbv[s]);
+          if (kb + kD < KB) load(s, kb + kD);
+        }
+      }
+    }
+    const float ysc = PT ? reinterpret_cast<const float*>(hs)[0] * (shared ? a.ss2[0] : a.s2[g]) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + lq * 4 + i;
+      if (r < rend) {
+        const float v = PT ? acc[i] * ysc : acc[i];
+        if (YBF16)
+          static_cast<uint16_t*>(y)[(int64_t)r * H + n0 + lr] = (uint16_t)f32_to_bf16(v);
+        else
+          static_cast<float*>(y)[(int64_t)r * H + n0 + lr] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm13_mx_stream(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq,
+                                   uint8_t* hs, hipStream_t s) {
+  gemm13_mx_stream<0><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, xs, hq, hs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm13_pt_stream(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
+                                   hipStream_t s) {
+  gemm13_mx_stream<1><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
+                                                                  reinterpret_cast<uint8_t*>(hamax));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_mx_stream(const GemmArgs& a, const uint8_t* hq, const uint8_t* hs, void* y, int y_dtype,
+                                  int pt, hipStream_t s) {
+  const int grid = device_cus() * 8;
+  if (pt) {
+    if (y_dtype == 1)
+      gemm2_mx_stream<1, 1><<<grid, 256, 0, s>>>(a, hq, hs, y);
+    else
+      gemm2_mx_stream<1, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
+  } else {
+    if (y_dtype == 1)
+      gemm2_mx_stream<0, 1><<<grid, 256, 0, s>>>(a, hq, hs, y);
+    else
+      gemm2_mx_stream<0, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe355

@@ -422,8 +422,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_mx(GemmArgs a, const u
 // The Down kernel needs H % 256 == 0 (weight-row tile); Gate-Up always tiles
 // (2*I % 256 == 0 since I % 128 == 0).
 
+// Groups of up to 16 rows on average take the weight-streaming kernels
+// (gemm_mx_stream.hip); larger ones these tiles.
 hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq, uint8_t* hs,
                             int* sync, hipStream_t s) {
+  if (small_groups(a)) return launch_gemm13_mx_stream(a, xq, xs, hq, hs, s);
   clear_sync_mx<<<1, 64, 0, s>>>(sync, nullptr);
   gemm_tiled_mx<0, 0><<<device_cus(), kThreads, 0, s>>>(a, xq, xs, hq, hs,
                                                        round_barrier(a, kTM) ? sync : nullptr);
@@ -433,6 +436,7 @@ hipError_t launch_gemm13_mx(const GemmArgs& a, const uint8_t* xq, const uint8_t*
 hipError_t launch_gemm13_pt(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
                             int* sync, hipStream_t s) {
   clear_sync_mx<<<1, 64, 0, s>>>(sync, reinterpret_cast<unsigned*>(hamax));
+  if (small_groups(a)) return launch_gemm13_pt_stream(a, xq, xs, h, hamax, s);
   gemm_tiled_mx<0, 0, 1><<<device_cus(), kThreads, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
                                                           reinterpret_cast<uint8_t*>(hamax),
                                                           round_barrier(a, kTM) ? sync : nullptr);
@@ -442,6 +446,7 @@ hipError_t launch_gemm13_pt(const GemmArgs& a, const uint8_t* xq, const float* x
 hipError_t launch_gemm2_pt(const GemmArgs& a, const uint8_t* hq, const float* hs, void* y, int y_dtype,
                            hipStream_t s) {
   const uint8_t* hsb = reinterpret_cast<const uint8_t*>(hs);
+  if (small_groups(a)) return launch_gemm2_mx_stream(a, hq, hsb, y, y_dtype, 1, s);
   if (y_dtype == 1)
     gemm_tiled_mx<1, 1, 1><<<device_cus(), kThreads, 0, s>>>(a, hq, hsb, y, nullptr, nullptr);
   else
@@ -451,6 +456,7 @@ hipError_t launch_gemm2_pt(const GemmArgs& a, const uint8_t* hq, const float* hs
 
 hipError_t launch_gemm2_mx(const GemmArgs& a, const uint8_t* hq, const uint8_t* hs, void* y, int y_dtype,
                            hipStream_t s) {
+  if (small_groups(a)) return launch_gemm2_mx_stream(a, hq, hs, y, y_dtype, 0, s);
   if (y_dtype == 1)
     gemm_tiled_mx<1, 1><<<device_cus(), kThreads, 0, s>>>(a, hq, hs, y, nullptr, nullptr);
   else

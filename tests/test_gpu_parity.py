@@ -81,6 +81,8 @@ MX_SMALL = [
     W("mx-ragged", T=37, H=256, E=8, k=3, I=384, shared=0, wtype="mxfp8", seed=25),
     W("mx-zipf", T=400, H=256, E=32, k=8, I=256, shared=1, wtype="mxfp8", bias="all", seed=26),
     W("mx-tiny-groups", T=16, H=512, E=64, k=8, I=256, shared=1, wtype="mxfp8", seed=27),
+    # weight-streaming kernels (up to 16 rows per expert on average), ragged K and chunks
+    W("mx-stream", T=33, H=768, E=40, k=6, I=384, shared=1, wtype="mxfp8", bias="mix", bias_frac=0.3, seed=29),
 ]
 
 
@@ -126,6 +128,7 @@ PT_SMALL = [
     W("pt-ragged", T=37, H=256, E=8, k=3, I=384, shared=0, wtype="fp8t", seed=35),
     W("pt-zipf", T=400, H=256, E=32, k=8, I=256, shared=1, wtype="fp8t", bias="all", seed=36),
     W("pt-tiny-groups", T=16, H=512, E=64, k=8, I=256, shared=1, wtype="fp8t", seed=37),
+    W("pt-stream", T=33, H=768, E=40, k=6, I=384, shared=1, wtype="fp8t", bias="mix", bias_frac=0.3, seed=48),
 ]
 
 
@@ -279,7 +282,8 @@ def test_fp8_codec_exhaustive_over_bf16():
 @pytest.mark.parametrize("name,ydt", [("tiny", torch.float32), ("decode", torch.float32),
                                       ("prefill", torch.bfloat16), ("fp8", torch.float32),
                                       ("mxfp8", torch.float32), ("fp8t", torch.float32),
-                                      ("router", torch.bfloat16)])
+                                      ("router", torch.bfloat16), ("decode_fp8", torch.float32),
+                                      ("decode_mxfp8", torch.float32), ("decode_fp8t", torch.bfloat16)])
 def test_layer_configs(name, ydt):
     wl = workloads.WORKLOADS[name]
     d = _inputs(wl)

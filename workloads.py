@@ -18,6 +18,9 @@ Workloads (shapes and distributions of the five layer configurations):
            weights [E,H], 30% of tokens carry the Zipf logit bias
   fp8perm  the fp8 workload with the Zipf ranks permuted (seeded), so the hot
            experts sit at scattered expert indices instead of 0, 1, 2, ...
+  decode_fp8, decode_mxfp8, decode_fp8t
+           the decode shape and routing with 128x128-block, MXFP8 and
+           per-tensor FP8 weights
 Distributions: weights bf16 ~N(0, 0.02), activations bf16 ~N(0, 1), router
 logits fp32 ~N(0, 1), router weights fp32 ~N(0, 0.01).  Values are drawn in
 fp32 and rounded to bf16 by torch's round-to-nearest-even conversion.  The
@@ -77,6 +80,11 @@ WORKLOADS = {
                        bias_frac=0.3, router=True, seed=1005),
     "fp8perm": Workload("fp8perm", T=4096, H=6144, E=256, k=8, I=2048, shared=1, wtype="fp8",
                         bias="all", bias_perm=77, seed=1004),
+    "decode_fp8": Workload("decode_fp8", T=64, H=4096, E=256, k=8, I=1536, shared=1, wtype="fp8", seed=1002),
+    "decode_mxfp8": Workload("decode_mxfp8", T=64, H=4096, E=256, k=8, I=1536, shared=1, wtype="mxfp8",
+                             seed=1002),
+    "decode_fp8t": Workload("decode_fp8t", T=64, H=4096, E=256, k=8, I=1536, shared=1, wtype="fp8t",
+                            seed=1002),
 }
 
 
