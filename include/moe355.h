@@ -321,6 +321,14 @@ int moe_forward_noalloc(const moe_experts_t* ex, const moe_forward_args_t* args,
  * chain kernel ([router_gemm] first when logits is NULL).
  * Envelope: wtype MOE_W_BF16 and at most 16 routed rows per expert on average
  * (T*k <= 16*E); anything else returns MOE_EUNSUPPORTED with nothing enqueued.
+ * When it pays (measured on MI355X): only for small batches launched eagerly,
+ * where the host's launch rate is the bottleneck (16 tokens, H 256, E 8, top-2:
+ * about 23 us against 38-45 us for five eager stage launches).  With the
+ * stages replayed from a HIP graph, or from decode-sized batches on (64 tokens,
+ * H 4096, E 256, top-8: 1.58 ms against 1.32 ms), moe_forward is faster: the
+ * chain's device-side hand-overs cost more than graph launches, and its one
+ * register allocation, sized for Gate-Up, leaves the Down phase fewer bytes in
+ * flight than the stand-alone Down kernel.
  *
  * Residency: the chain kernel's grid is sized to what the device holds at
  * once, and it completes only if all of its workgroups are resident together
