@@ -233,6 +233,36 @@ def cpu_baseline(wl, d, b, budget_s):
                       + ("; h scale from the sampled pairs" if wl.wtype == "fp8t" else "")}
 
 
+def router_gemm_only(T: int) -> None:
+    """The split-BF16 router GEMM on its own: x [T, H] bf16 ~N(0, 1), router
+    weights [E, H] fp32 ~N(0, 0.01) split on the device, H and E of the router
+    workload; prints one JSON line with the average time per call."""
+    import expert_layer_amd as moe
+    wl = workloads.WORKLOADS["router"]
+    H, E = wl.H, wl.E
+    g = torch.Generator(device="cuda:0").manual_seed(wl.seed)
+    x = torch.randn((T, H), generator=g, device="cuda:0").to(torch.bfloat16)
+    w = 0.01 * torch.randn((E, H), generator=g, device="cuda:0")
+    hi = torch.empty((E, H), dtype=torch.bfloat16, device="cuda:0")
+    lo = torch.empty_like(hi)
+    logits = torch.empty((T, E), device="cuda:0")
+    moe.moe_router_split(w, hi, lo)
+    for _ in range(3):
+        moe.moe_router_gemm(x, hi, lo, logits)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    t0.record()
+    for _ in range(n):
+        moe.moe_router_gemm(x, hi, lo, logits)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1000.0 / n
+    print(json.dumps({"router_gemm_us": round(us, 2), "T": T, "H": H, "E": E, "calls": n,
+                      "tflops": round(2 * 2 * T * H * E / us / 1e6, 1),
+                      "x_bytes": T * H * 2, "split_weight_bytes": 2 * E * H * 2}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,7 +280,13 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, run a plain device copy of BYTES bytes 5 times (used to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--router-gemm", type=int, default=0, metavar="T",
+                    help="instead of the layer, time the split-BF16 router GEMM alone on T tokens at the router "
+                         "workload's hidden size and expert count (10 calls after 3 warm-up; for its counters)")
     args = ap.parse_args()
+    if args.router_gemm:
+        router_gemm_only(args.router_gemm)
+        return
     if args.copy_calibration:
         n = args.copy_calibration
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")

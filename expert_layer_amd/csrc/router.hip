@@ -26,11 +26,16 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // stage of 64 k, the 128 token rows and the 256 weight rows (128 hi, then 128
 // lo) are one whole 128-byte line each, staged into LDS with the gfx950
 // direct-to-LDS loads (8 rows per load instruction) in a ring of 2 stages
-// (2 x 48 KB).  The activations are read once per 128 experts, the split
-// weights once per 128 tokens.  Eight waves in a 2 (tokens) x 4 (experts)
-// grid; wave (wm, wn) owns tokens 64*wm .. +63 and experts 32*wn .. +31 of
-// the tile, i.e. 4 x 2 MFMA tiles for each of hi and lo.  Rows past T or E
-// load the last valid row and are not stored.
+// (2 x 48 KB).  Eight waves in a 2 (tokens) x 4 (experts) grid; wave (wm, wn)
+// owns tokens 64*wm .. +63 and experts 32*wn .. +31 of the tile, i.e. 4 x 2
+// MFMA tiles for each of hi and lo.  Rows past T or E load the last valid row
+// and are not stored.
+//
+// The activations cross HBM once: the expert tiles of one token tile are
+// consecutive workgroups on one XCD (workgroups are dealt to the 8 XCDs round
+// robin), so they start together and the second reads the token rows from
+// that XCD's L2.  Workgroup b runs token tile 8 * (j / ET) + b % 8 and expert
+// tile j % ET, with j = b / 8 and ET expert tiles; token tiles past T exit.
 constexpr int kRT = 128;           // tokens per tile
 constexpr int kRE = 128;           // experts per tile
 constexpr int kRK = 64;            // k per stage
@@ -63,8 +68,11 @@ __global__ __launch_bounds__(kRThreads, 1) void router_gemm_kernel(const uint16_
   const int wm = wave >> 2, wn = wave & 3;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
   const int lrow = lane >> 3, lslot = lane & 7;   // direct-load role: 8 rows x 8 slots per load
-  const int64_t t0 = (int64_t)blockIdx.x * kRT;
-  const int e0 = blockIdx.y * kRE;
+  const int ET = (E + kRE - 1) / kRE;
+  const int j = blockIdx.x >> 3;
+  const int64_t t0 = ((int64_t)8 * (j / ET) + (blockIdx.x & 7)) * kRT;
+  const int e0 = (j % ET) * kRE;
+  if (t0 >= T) return;   // whole workgroup: no barrier is reached
 
   // A: load i (0, 1) of this wave fills tile rows 8*(2*wave+i) + lane/8
   int64_t a_off[2];
@@ -165,8 +173,11 @@ hipError_t launch_router_split(const float* w, uint16_t* hi, uint16_t* lo, int64
 
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* hi, const uint16_t* lo, float* logits,
                               int64_t T, int H, int E, hipStream_t s) {
-  const dim3 grid((unsigned)((T + kRT - 1) / kRT), (unsigned)((E + kRE - 1) / kRE));
-  router_gemm_kernel<<<grid, kRThreads, 0, s>>>(x, hi, lo, logits, T, H, E);
+  // token tiles rounded up to a multiple of 8, times the expert tiles
+  const int64_t tt = (T + kRT - 1) / kRT;
+  const int64_t nblk = ((tt + 7) / 8) * 8 * ((E + kRE - 1) / kRE);
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  router_gemm_kernel<<<(unsigned)nblk, kRThreads, 0, s>>>(x, hi, lo, logits, T, H, E);
   return hipGetLastError();
 }
 

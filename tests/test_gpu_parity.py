@@ -444,3 +444,30 @@ def test_combine_rmsnorm_stage(ydt):
     assert np.all(np.abs(got_s - s_ref) <= 2.0 ** -8 * np.abs(s_ref) + 1e-6 * np.abs(s_ref).max())
     assert np.all(np.abs(got - out_ref) <= 2.0 ** -8 * np.abs(out_ref) + 1e-6 * np.abs(out_ref).max())
     log(f"  combine+rmsnorm: max|out-ref| {np.abs(got - out_ref).max():.3e}, max|ref| {np.abs(out_ref).max():.3e}")
+
+
+@pytest.mark.parametrize("T,H,E", [(1100, 256, 200), (1, 128, 1000), (2049, 384, 64), (8 * 128 + 1, 128, 129)],
+                         ids=["T1100-E200", "T1-E1000", "T2049-E64", "T1025-E129"])
+def test_router_gemm_tile_map(T, H, E):
+    """Split-BF16 router GEMM on its own, at token-tile counts past one per XCD
+    and expert-tile counts 1..8: every logit written once (the buffer starts as
+    NaN), split bits equal to the oracle's, logits within 1e-5 max|ref| of fp64."""
+    import expert_layer_amd as moe
+    from oracle import oracle as orc
+    g = torch.Generator(device="cuda").manual_seed(T * 7 + E)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    w = 0.01 * torch.randn((E, H), generator=g, device="cuda")
+    hi = torch.empty((E, H), dtype=torch.bfloat16, device="cuda")
+    lo = torch.empty_like(hi)
+    logits = torch.full((T, E), float("nan"), device="cuda")
+    moe.moe_router_split(w, hi, lo)
+    moe.moe_router_gemm(x, hi, lo, logits)
+    torch.cuda.synchronize()
+    rhi, rlo = orc.router_split(w.cpu().numpy())
+    assert np.array_equal(workloads.bits(hi), rhi) and np.array_equal(workloads.bits(lo), rlo)
+    got = logits.double().cpu().numpy()
+    assert not np.isnan(got).any(), "logits left unwritten"
+    ref = orc.router_logits(workloads.bits(x), w.cpu().numpy())
+    err = np.abs(got - ref).max()
+    log(f"  router T={T} H={H} E={E}: max|d| {err:.3e}, max|ref| {np.abs(ref).max():.3e}")
+    assert err <= 1e-5 * np.abs(ref).max()
