@@ -150,6 +150,13 @@ __global__ __launch_bounds__(512) void gemm13_fp8_stream(GemmArgs a, const uint8
 }
 
 // ---------------------------------------------------------------- Down
+// A wave owns one 16-row chunk x 16 output columns.  Each K block's scales
+// travel with its codes, kD blocks in flight: loads retire in issue order, so
+// a scale loaded at its point of use would make the block wait for all the
+// blocks prefetched after it (Down 0.39 -> 0.30 ms at decode size; the
+// Gate-Up measured 1 % slower this way and keeps its scale loads at the point
+// of use).  Rows past the chunk's end read the chunk's last row (their
+// results are never stored), so no load sits behind a per-lane condition.
 template <int YBF16>
 __global__ __launch_bounds__(256) void gemm2_fp8_stream(GemmArgs a, const uint8_t* __restrict__ hq,
                                                         const float* __restrict__ hs,
@@ -163,7 +170,6 @@ __global__ __launch_bounds__(256) void gemm2_fp8_stream(GemmArgs a, const uint8_
   const int64_t items = (int64_t)nchunks * NT;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const i32x8_t zero = {};
 
   for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items; it += nwaves) {
     const int c = (int)(it / NT);
@@ -176,40 +182,32 @@ __global__ __launch_bounds__(256) void gemm2_fp8_stream(GemmArgs a, const uint8_
     const uint8_t* w2 = shared ? static_cast<const uint8_t*>(a.sw2) : static_cast<const uint8_t*>(a.w2) + g * mat;
     const float* s2 = (shared ? a.ss2 : a.s2 + g * blk) + (int64_t)(n0 / 128) * KB;
     const uint8_t* bp = w2 + (int64_t)(n0 + lr) * I + lq * 32;
-    const int ra = r0 + lr;
-    const uint8_t* ap = ra < rend ? hq + (int64_t)ra * I + lq * 32 : nullptr;
+    const uint8_t* ap = hq + (int64_t)min(r0 + lr, rend - 1) * I + lq * 32;
     const float* hsr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + lq * 4 + i;
-      hsr[i] = r < rend ? hs + (int64_t)r * KB : nullptr;
-    }
+    for (int i = 0; i < 4; ++i) hsr[i] = hs + (int64_t)min(r0 + lq * 4 + i, rend - 1) * KB;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     i32x8_t av[kD], bw[kD];
+    float hv[kD][4], sw[kD];
+    auto load = [&](int s, int kb) {
+      av[s] = ld32(ap + 128 * kb);
+      bw[s] = ld32(bp + 128 * kb);
 #pragma unroll
-    for (int s = 0; s < kD; ++s) {
-      if (s < KB) {
-        av[s] = ap ? ld32(ap + 128 * s) : zero;
-        bw[s] = ld32(bp + 128 * s);
-      }
-    }
+      for (int i = 0; i < 4; ++i) hv[s][i] = hsr[i][kb];
+      sw[s] = s2[kb];
+    };
+#pragma unroll
+    for (int s = 0; s < kD; ++s)
+      if (s < KB) load(s, s);
     for (int kb0 = 0; kb0 < KB; kb0 += kD) {
 #pragma unroll
       for (int s = 0; s < kD; ++s) {
         const int kb = kb0 + s;
         if (kb < KB) {
           const f32x4_t p = mfma_fp8(av[s], bw[s]);
-          const float sw = s2[kb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float hsv = hsr[i] ? hsr[i][kb] : 0.0f;
-            acc[i] = __builtin_fmaf(hsv * sw, p[i], acc[i]);
-          }
-          const int kn = kb + kD;
-          if (kn < KB) {
-            av[s] = ap ? ld32(ap + 128 * kn) : zero;
-            bw[s] = ld32(bp + 128 * kn);
-          }
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(hv[s][i] * sw[s], p[i], acc[i]);
+          if (kb + kD < KB) load(s, kb + kD);
         }
       }
     }

@@ -33,6 +33,40 @@ namespace {
 
 constexpr int kD = 2;          // K blocks of 128 in flight per wave
 constexpr int kWaves13 = 4;    // Gate-Up workgroup: 4 waves x 32 columns
+constexpr int kStgKB13 = 48;   // staged MX scales: K blocks per row at most (Gate-Up: H <= 6144)
+constexpr int kStgKB2 = 32;    // (Down: I <= 4096)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// gfx950 direct-to-LDS load: lane l's 16 bytes land at lds_base + 16 l
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// MX scale staging.  A scale byte is read once per K block, and with the
+// weight codes streaming past, its 128-byte line no longer sits in L2 by the
+// next block (the Gate-Up read about 1.2x its algorithmic bytes that way).
+// So each wave copies the scale rows of its fragments into its own LDS region
+// once per item, with direct-to-LDS loads issued before the item's first code
+// loads: per fragment row (16 rows), K blocks in groups of 16, lane (lr, q)
+// of a copy holding the 4 scale bytes of blocks 16 g + 4 q .. +3 of row lr.
+// Only the wave itself reads its region, and LDS operations of one wave run
+// in order, so no barrier is needed; the next item's copy is issued after the
+// last block's scales were consumed.  Needs K % 512 == 0 (whole 16-byte pieces).
+template <int G16>
+__device__ __forceinline__ void stage_row(i32x4_t* region, int frow, const uint8_t* row, int KB, int lq) {
+  for (int g = 0; g < (KB + 15) / 16; ++g) {
+    const int kb = min(16 * g + 4 * lq, KB - 4);   // lanes past the row copy a valid piece (never read)
+    load_lds16(row + 4 * kb, region + (frow * G16 + g) * 64);
+  }
+}
+
+template <int G16>
+__device__ __forceinline__ int staged_byte(const i32x4_t* region, int frow, int kb, int lr, int lq) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(region + (frow * G16 + (kb >> 4)) * 64 + lr + 16 * ((kb & 15) >> 2));
+  return p[4 * (kb & 3) + lq];
+}
 
 __device__ __forceinline__ i32x8_t ld_frag(const uint8_t* p) {
   // the two 16-byte pieces of a lane: bytes 0..15 and 64..79 from p
@@ -53,21 +87,26 @@ __device__ __forceinline__ int scale_byte(const uint8_t* row, int kb, int lq) {
 }
 
 // ---------------------------------------------------------------- Gate-Up
-template <int PT>
+template <int PT, int STG>
 __global__ __launch_bounds__(64 * kWaves13) void gemm13_mx_stream(GemmArgs a, const uint8_t* __restrict__ xq,
                                                                   const uint8_t* __restrict__ xs,
                                                                   void* __restrict__ hout,
                                                                   uint8_t* __restrict__ hs) {
   __shared__ ChunkTable tab;
+  constexpr int G16 = kStgKB13 / 16;
+  // staged scales: per wave, fragment rows 0-3 (weights), 4 (activations)
+  __shared__ i32x4_t stg[STG ? kWaves13 * 5 * G16 * 64 : 1];
   const int G = a.E + (a.has_shared ? 1 : 0);
   const int nchunks = build_chunks(tab, a.offsets, G, 16);
   const int H = a.H, I = a.I;
   const int KB = H / 128, NB = I / 128, HM = H / 32;
   const int64_t items = (int64_t)nchunks * NB;
   const int64_t P = a.T * a.k;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
   const i32x8_t zero = {};
   float hmax = 0.0f;   // per-tensor: running max |h| of this thread
+  i32x4_t* region = stg + (STG ? wave * 5 * G16 * 64 : 0);
 
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int c = (int)(it / NB);
@@ -103,20 +142,29 @@ __global__ __launch_bounds__(64 * kWaves13) void gemm13_mx_stream(GemmArgs a, co
       ap = xq + t * H + 16 * lq;
       if (!PT) as = xs + t * HM;
     }
+    if (STG) {
+      // rows past the chunk copy the chunk's last row's scales (never used)
+      const int rc = min(ra, rend - 1);
+      const int64_t tc = rc < P ? (int64_t)(a.slot_pair[rc] / a.k) : (int64_t)rc - P;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) stage_row<G16>(region, f, bs[f], KB, lq);
+      stage_row<G16>(region, 4, xs + tc * HM, KB, lq);
+    }
     f32x4_t acc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // codes and scale bytes of kD K blocks in flight (the scales travel with
-    // their codes, so their latency is hidden as well)
+    // their codes, so their latency is hidden as well; staged scales are read
+    // from LDS when their block is computed)
     i32x8_t av[kD], bv[kD][4];
     int sav[kD], sbv[kD][4];
     auto load = [&](int s, int kb) {
       av[s] = ap ? ld_frag(ap + 128 * kb) : zero;
-      sav[s] = PT ? 127 : scale_byte(as, kb, lq);
+      if (!STG) sav[s] = PT ? 127 : scale_byte(as, kb, lq);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         bv[s][f] = ld_frag(bp[f] + 128 * kb);
-        sbv[s][f] = PT ? 127 : scale_byte(bs[f], kb, lq);
+        if (!STG) sbv[s][f] = PT ? 127 : scale_byte(bs[f], kb, lq);
       }
     };
 #pragma unroll
@@ -127,6 +175,11 @@ __global__ __launch_bounds__(64 * kWaves13) void gemm13_mx_stream(GemmArgs a, co
       for (int s = 0; s < kD; ++s) {
         const int kb = kb0 + s;
         if (kb < KB) {
+          if (STG) {
+            sav[s] = staged_byte<G16>(region, 4, kb, lr, lq);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) sbv[s][f] = staged_byte<G16>(region, f, kb, lr, lq);
+          }
 #pragma unroll
           for (int f = 0; f < 4; ++f) acc[f] = mfma_mx(av[s], bv[s][f], acc[f], sav[s], sbv[s][f]);
           if (kb + kD < KB) load(s, kb + kD);
@@ -182,10 +235,13 @@ __global__ __launch_bounds__(64 * kWaves13) void gemm13_mx_stream(GemmArgs a, co
 }
 
 // ---------------------------------------------------------------- Down
-template <int PT, int YBF16>
+template <int PT, int YBF16, int STG>
 __global__ __launch_bounds__(256) void gemm2_mx_stream(GemmArgs a, const uint8_t* __restrict__ hq,
                                                        const uint8_t* __restrict__ hs, void* __restrict__ y) {
   __shared__ ChunkTable tab;
+  constexpr int G16 = kStgKB2 / 16;
+  // staged scales: per wave, fragment row 0 (weights), 1 (h rows)
+  __shared__ i32x4_t stg[STG ? 4 * 2 * G16 * 64 : 1];
   const int G = a.E + (a.has_shared ? 1 : 0);
   const int nchunks = build_chunks(tab, a.offsets, G, 16);
   const int H = a.H, I = a.I;
@@ -193,10 +249,12 @@ __global__ __launch_bounds__(256) void gemm2_mx_stream(GemmArgs a, const uint8_t
   const int NT = H / 16;
   const int64_t items = (int64_t)nchunks * NT;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   const i32x8_t zero = {};
+  i32x4_t* region = stg + (STG ? wave * 2 * G16 * 64 : 0);
 
-  for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items; it += nwaves) {
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < items; it += nwaves) {
     const int c = (int)(it / NT);
     const int n0 = (int)(it % NT) * 16;
     const int g = chunk_group(tab, G, c);
@@ -214,14 +272,20 @@ __global__ __launch_bounds__(256) void gemm2_mx_stream(GemmArgs a, const uint8_t
     const int ra = r0 + lr;
     const uint8_t* ap = ra < rend ? hq + (int64_t)ra * I + 16 * lq : nullptr;
     const uint8_t* as = (!PT && ra < rend) ? hs + (int64_t)ra * IM : nullptr;
+    if (STG) {
+      stage_row<G16>(region, 0, bs, KB, lq);
+      stage_row<G16>(region, 1, hs + (int64_t)min(ra, rend - 1) * IM, KB, lq);
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     i32x8_t av[kD], bw[kD];
     int sav[kD], sbv[kD];
     auto load = [&](int s, int kb) {
       av[s] = ap ? ld_frag(ap + 128 * kb) : zero;
       bw[s] = ld_frag(bp + 128 * kb);
-      sav[s] = PT ? 127 : scale_byte(as, kb, lq);
-      sbv[s] = PT ? 127 : scale_byte(bs, kb, lq);
+      if (!STG) {
+        sav[s] = PT ? 127 : scale_byte(as, kb, lq);
+        sbv[s] = PT ? 127 : scale_byte(bs, kb, lq);
+      }
     };
 #pragma unroll
     for (int s = 0; s < kD; ++s)
@@ -231,6 +295,10 @@ __global__ __launch_bounds__(256) void gemm2_mx_stream(GemmArgs a, const uint8_t
       for (int s = 0; s < kD; ++s) {
         const int kb = kb0 + s;
         if (kb < KB) {
+          if (STG) {
+            sav[s] = staged_byte<G16>(region, 1, kb, lr, lq);
+            sbv[s] = staged_byte<G16>(region, 0, kb, lr, lq);
+          }
           acc = mfma_mx(av[s], bw[s], acc, sav[s], sbv[s]);
           if (kb + kD < KB) load(s, kb + kD);
         }
@@ -255,13 +323,16 @@ __global__ __launch_bounds__(256) void gemm2_mx_stream(GemmArgs a, const uint8_t
 
 hipError_t launch_gemm13_mx_stream(const GemmArgs& a, const uint8_t* xq, const uint8_t* xs, uint8_t* hq,
                                    uint8_t* hs, hipStream_t s) {
-  gemm13_mx_stream<0><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, xs, hq, hs);
+  if (a.H % 512 == 0 && a.H / 128 <= kStgKB13)
+    gemm13_mx_stream<0, 1><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, xs, hq, hs);
+  else
+    gemm13_mx_stream<0, 0><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, xs, hq, hs);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm13_pt_stream(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
                                    hipStream_t s) {
-  gemm13_mx_stream<1><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
+  gemm13_mx_stream<1, 0><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
                                                                   reinterpret_cast<uint8_t*>(hamax));
   return hipGetLastError();
 }
@@ -271,14 +342,19 @@ hipError_t launch_gemm2_mx_stream(const GemmArgs& a, const uint8_t* hq, const ui
   const int grid = device_cus() * 8;
   if (pt) {
     if (y_dtype == 1)
-      gemm2_mx_stream<1, 1><<<grid, 256, 0, s>>>(a, hq, hs, y);
+      gemm2_mx_stream<1, 1, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
     else
-      gemm2_mx_stream<1, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
+      gemm2_mx_stream<1, 0, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
+  } else if (a.I % 512 == 0 && a.I / 128 <= kStgKB2) {
+    if (y_dtype == 1)
+      gemm2_mx_stream<0, 1, 1><<<grid, 256, 0, s>>>(a, hq, hs, y);
+    else
+      gemm2_mx_stream<0, 0, 1><<<grid, 256, 0, s>>>(a, hq, hs, y);
   } else {
     if (y_dtype == 1)
-      gemm2_mx_stream<0, 1><<<grid, 256, 0, s>>>(a, hq, hs, y);
+      gemm2_mx_stream<0, 1, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
     else
-      gemm2_mx_stream<0, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
+      gemm2_mx_stream<0, 0, 0><<<grid, 256, 0, s>>>(a, hq, hs, y);
   }
   return hipGetLastError();
 }

@@ -83,6 +83,10 @@ MX_SMALL = [
     W("mx-tiny-groups", T=16, H=512, E=64, k=8, I=256, shared=1, wtype="mxfp8", seed=27),
     # weight-streaming kernels (up to 16 rows per expert on average), ragged K and chunks
     W("mx-stream", T=33, H=768, E=40, k=6, I=384, shared=1, wtype="mxfp8", bias="mix", bias_frac=0.3, seed=29),
+    # streaming kernels with the scale rows staged in LDS (K % 512 == 0): one
+    # partly used group of 16 K blocks, and a second, partly used group
+    W("mx-stream-staged", T=40, H=1536, E=48, k=6, I=1536, shared=1, wtype="mxfp8", seed=45),
+    W("mx-stream-staged2", T=24, H=2560, E=32, k=4, I=2048, shared=1, wtype="mxfp8", bias="all", seed=46),
 ]
 
 
