@@ -68,6 +68,10 @@ FP8_SMALL = [
     W("fp8-ragged", T=37, H=384, E=8, k=3, I=384, shared=0, wtype="fp8", seed=22),
     W("fp8-zipf", T=400, H=256, E=32, k=8, I=256, shared=1, wtype="fp8", bias="all", seed=23),
     W("fp8-zipf-perm", T=500, H=256, E=32, k=8, I=256, shared=1, wtype="fp8", bias="all", bias_perm=6, seed=28),
+    # weight-streaming kernels (up to 16 rows per expert on average) at each
+    # K-blocks-in-flight depth: Gate-Up KB 8 / 5, Down KB 6 / 4
+    W("fp8-stream", T=33, H=1024, E=40, k=6, I=768, shared=1, wtype="fp8", bias="mix", bias_frac=0.3, seed=47),
+    W("fp8-stream2", T=20, H=640, E=24, k=4, I=512, shared=1, wtype="fp8", seed=49),
 ]
 
 
