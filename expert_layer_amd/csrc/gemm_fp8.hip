@@ -260,7 +260,9 @@ __global__ __launch_bounds__(256) void gemm2_fp8_stream(GemmArgs a, const uint8_
 hipError_t launch_gemm13_fp8(const GemmArgs& a, const uint8_t* xq, const float* xs, uint8_t* hq, float* hs,
                              hipStream_t s) {
   if (large_groups(a) && tiled_fp8_gemm13_ok(a)) return launch_gemm13_fp8_tiled(a, xq, xs, hq, hs, s);
-  const int KB = a.H / 128, grid = device_cus() * 4;
+  // one workgroup per CU, the number resident (decode shape: 0.433 ms against
+  // 0.444 ms with a grid of four per CU)
+  const int KB = a.H / 128, grid = device_cus();
   if (KB % 4 == 0)
     gemm13_fp8_stream<4><<<grid, 512, 0, s>>>(a, xq, xs, hq, hs);
   else if (KB % 2 == 0)

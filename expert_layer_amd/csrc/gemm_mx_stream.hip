@@ -373,7 +373,10 @@ hipError_t launch_gemm13_mx_stream(const GemmArgs& a, const uint8_t* xq, const u
 
 hipError_t launch_gemm13_pt_stream(const GemmArgs& a, const uint8_t* xq, const float* xs, float* h, float* hamax,
                                    hipStream_t s) {
-  gemm13_mx_stream<1, 0, 2><<<device_cus() * 8, 64 * kWaves13, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
+  // two workgroups per CU, as many as the MX kernel's LDS copy allows: the
+  // per-tensor kernel could hold three, but ran 0.444 ms at the decode shape
+  // with two against 0.455 with three and 0.485 with a grid of eight per CU
+  gemm13_mx_stream<1, 0, 2><<<device_cus() * 2, 64 * kWaves13, 0, s>>>(a, xq, reinterpret_cast<const uint8_t*>(xs), h,
                                                                   reinterpret_cast<uint8_t*>(hamax));
   return hipGetLastError();
 }
