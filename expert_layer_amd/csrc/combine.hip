@@ -18,9 +18,9 @@ namespace {
 
 constexpr int kThreads = 256;
 // Small batches (T < 2048, latency-bound): 8 y terms are loaded before they
-// are summed (decode combine 10.7 -> 8.5 us).  Large batches keep one load
-// per term in flight at the higher occupancy of the smaller register set,
-// which measured faster there.  Both sum in the same order.
+// are summed (decode combine 10.7 -> 8.5 us).  Large batches load 4 at a time
+// (1, 2 and 4 measured the same there; the RMSNorm variant keeps 1).  All
+// sum in the same order.
 constexpr int64_t kBatchBelowT = 2048;
 
 template <int YBF16, int BATCH>
@@ -128,9 +128,9 @@ hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pair_slot, 
   const bool small = T < kBatchBelowT;
   auto go = [&](auto kern) { kern<<<(unsigned)T, kThreads, 0, s>>>(y, pair_slot, w, T, k, H, has_shared, out); };
   if (y_dtype == 1) {
-    if (small) go(combine_kernel<1, 8>); else go(combine_kernel<1, 1>);
+    if (small) go(combine_kernel<1, 8>); else go(combine_kernel<1, 4>);
   } else {
-    if (small) go(combine_kernel<0, 8>); else go(combine_kernel<0, 1>);
+    if (small) go(combine_kernel<0, 8>); else go(combine_kernel<0, 4>);
   }
   return hipGetLastError();
 }
