@@ -47,15 +47,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """Hash of every kernel source: counter figures are reported only for the sources they were taken on."""
+CSRC = os.path.join(ROOT, "expert_layer_amd", "csrc")
+
+
+def _include_closure(root):
+    """root and every csrc header it includes, directly or not."""
+    seen, todo = set(), [root]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.add(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            for line in fh:
+                line = line.strip()
+                if line.startswith("#include \""):
+                    todo.append(line.split('"')[1])
+    return sorted(seen)
+
+
+def kernel_source_hash(root=None):
+    """Hash of the kernel sources: with root (a .hip file of the library), of
+    that file and the headers it includes; without, of every source.  Counter
+    figures are reported only for the sources they were taken on."""
+    files = _include_closure(root) if root else sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "expert_layer_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode())
-                h.update(fh.read())
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -114,6 +134,8 @@ def load_traffic(name, src_hash):
         return None
     with open(path) as fh:
         t = json.load(fh)
+    if "kernel_file" in t:   # the kernel's own file and its headers
+        src_hash = kernel_source_hash(t["kernel_file"])
     if t.get("kernel_source_hash") != src_hash:
         return None
     return t.get("hbm_bytes_per_launch")
@@ -416,8 +438,8 @@ def main():
                 "frac": achieved / peak, "traffic": load_traffic(wl.name, src_hash)}
     if roof["traffic"] is not None:
         roof["traffic_source"] = (f"profiles/gemm13_{wl.name}_traffic.json: rocprofv3 FETCH_SIZE + WRITE_SIZE of "
-                                  "this kernel, calibrated on a device copy, taken on these kernel sources "
-                                  "(not measured in this run)")
+                                  "this kernel, calibrated on a device copy, taken on this kernel's current "
+                                  "source file and headers (not measured in this run)")
     roof["kernel"] = "gemm13"
     roof["per_launch"] = {"bytes": g13_bytes, "flops": g13_flops, "touched_experts": touched,
                           "avg_ms": stage_ms["gemm13"]}
