@@ -323,6 +323,10 @@ GRAPH_SHAPES = {
     "fp8": W("graph-f8", T=500, H=512, E=32, k=8, I=256, shared=1, wtype="fp8", bias="mix", bias_frac=0.3, seed=45),
     "mxfp8": W("graph-mx", T=500, H=512, E=32, k=8, I=256, shared=1, wtype="mxfp8", seed=46),
     "fp8t": W("graph-pt", T=500, H=512, E=32, k=8, I=256, shared=1, wtype="fp8t", seed=47),
+    # the weight-streaming FP8 kernels (decode-sized groups; MX with its scale rows staged in LDS)
+    "fp8-stream": W("graph-f8s", T=64, H=1024, E=64, k=8, I=512, shared=1, wtype="fp8", seed=50),
+    "mxfp8-stream": W("graph-mxs", T=64, H=1024, E=64, k=8, I=512, shared=1, wtype="mxfp8", seed=51),
+    "fp8t-stream": W("graph-pts", T=64, H=1024, E=64, k=8, I=512, shared=1, wtype="fp8t", seed=52),
 }
 
 
@@ -390,12 +394,16 @@ def test_concurrent_streams_match_serial():
     import expert_layer_amd as moe
     from expert_layer_amd.chain import Layer
     shapes = [W("cc-tiled", T=4096, H=512, E=8, k=4, I=256, shared=1, bias="mix", bias_frac=0.3, seed=81),
-              W("cc-stream", T=64, H=1024, E=64, k=8, I=256, shared=1, seed=82)]
+              W("cc-stream", T=64, H=1024, E=64, k=8, I=256, shared=1, seed=82),
+              # streaming MX (scale rows staged in LDS) and per-tensor FP8 (its h amax word in the workspace)
+              W("cc-mx-stream", T=64, H=1024, E=64, k=8, I=512, shared=1, wtype="mxfp8", seed=83),
+              W("cc-pt-stream", T=64, H=1024, E=64, k=8, I=512, shared=1, wtype="fp8t", seed=84)]
     runs = []
     for wl in shapes:
-        log(f"concurrent {wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I}")
+        log(f"concurrent {wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I} {wl.wtype}")
         d = _inputs(wl)
-        layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"])
+        layer = Layer.from_weights(d["w1"], d["w3"], d["w2"], d["sw1"], d["sw3"], d["sw2"], fp8=wl.wtype == "fp8",
+                                   mx=wl.wtype == "mxfp8", pt=wl.wtype == "fp8t")
         ydt = moe.MOE_DTYPE_F32
         ws = torch.empty(moe.moe_forward_workspace_bytes(layer.experts, wl.T, wl.k, ydt), dtype=torch.uint8,
                          device="cuda")
